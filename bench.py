@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Batched-decode PagedAttention benchmark on one MI355X.
+
+One step = one decode step of one attention layer over a synthetic batch:
+  * fp16 configs: paged_kv_append (this step's K/V rows into their slots)
+    -> paged_attn_decode (split-context partitions) -> paged_attn_reduce
+  * fused config (c4): the append also applies QK-RMSNorm + RoPE to q and k
+  * E4M3 config (c5): decode over FP8 KV -> reduce
+all on one HIP stream.  Inputs are resident in HBM before timing starts;
+R rotated copies of the pools, tables and q (>= 1 GiB touched between
+reuses) keep the 256 MB last-level cache from serving the KV.
+
+Prints one JSON line: value = KV-read GB/s over the whole step
+(algorithmic KV bytes / step time), plus steps/s, tokens/s, the decode
+kernel's roofline position (its own HIP-event time) and the CPU oracle
+baseline timed on this host.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from paged_kv_cache_208_amd import synth  # noqa: E402
+from paged_kv_cache_208_amd.roofline import HBM_GBPS  # noqa: E402
+
+METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + decode steps/s at B"
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="c2", choices=sorted(synth.CONFIGS))
+    p.add_argument("--partition-size", type=int, default=None)
+    p.add_argument("--rotate", type=int, default=None, help="copies of the inputs (default: auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="approximate CPU time budget for the oracle baseline")
+    return p.parse_args()
+
+
+# --------------------------------------------------------------------------- CPU baseline
+_CPU = {}
+
+
+def _oracle_worker(seqs):
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attn_ref
+
+    d, cfg = _CPU["d"], _CPU["cfg"]
+    with threadpool_limits(1):
+        attn_ref(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                 cfg.scale, k_scale=d["k_scale"], v_scale=d["v_scale"], seqs=seqs)
+    return len(seqs)
+
+
+def cpu_baseline(cfg, d, budget_s):
+    """Time the fp64 oracle on a bounded sample of the batch, parallel over
+    sequences with one single-threaded worker per host core (fork, before
+    the GPU is touched)."""
+    import multiprocessing as mp
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    _CPU.update(d=d, cfg=cfg)
+    lens = d["context_lens"].astype(np.int64)
+    # probe one sequence to size the sample to the budget
+    t0 = time.perf_counter()
+    _oracle_worker([int(np.argmin(np.abs(lens - lens.mean())))])
+    per_seq = max(time.perf_counter() - t0, 1e-4)
+    n = int(max(1, min(cfg.B, budget_s * cores / per_seq)))
+    seqs = list(range(n))
+    chunks = [seqs[i::cores] for i in range(cores) if seqs[i::cores]]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(len(chunks)) as pool:
+        t0 = time.perf_counter()
+        pool.map(_oracle_worker, chunks)
+        dt = time.perf_counter() - t0
+    kv = synth.kv_bytes(cfg, lens[:n])
+    frac = float(lens[:n].sum() / lens.sum())
+    return {
+        "value": kv / dt / 1e9,
+        "unit": "GB/s",
+        "cores": len(chunks),
+        "kind": "oracle",
+        "sample": f"{n} of {cfg.B} sequences ({frac:.1%} of the step's KV tokens), fp64 numpy, "
+                  f"one single-threaded worker per core",
+        "seconds": dt,
+        "step_seconds_extrapolated": dt / frac,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# --------------------------------------------------------------------------- GPU run
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(sequences and kv heads shard across GPUs with no exchange; see the design "
+              "notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = synth.CONFIGS[args.config]
+    if args.partition_size is not None:
+        cfg = cfg.replace(partition_size=args.partition_size)
+    t0 = time.perf_counter()
+    d = synth.generate(cfg)
+    print(f"# generated {cfg.name} in {time.perf_counter() - t0:.1f}s: B={cfg.B} "
+          f"Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} kv={cfg.kv_dtype} PS={cfg.partition_size} "
+          f"NB={d['nb']}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, d, args.cpu_seconds)
+        print(f"# cpu baseline: {cpu['value']:.3f} GB/s on {cpu['cores']} cores "
+              f"({cpu['seconds']:.1f}s)", file=sys.stderr, flush=True)
+
+    import torch
+
+    from paged_kv_cache_208_amd import _lib
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+
+    def up(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    base = {k: up(v) for k, v in d.items() if isinstance(v, np.ndarray)}
+    footprint = sum(t.numel() * t.element_size() for t in base.values())
+    R = args.rotate or max(2, math.ceil(ROTATE_BYTES / footprint))
+    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+    B, Hq, D = d["q"].shape
+    PS = cfg.partition_size
+    P = _lib.max_partitions_for(cfg.mbs, PS)
+    ws = _lib.alloc_partials(B, Hq, D, P, dev) if PS else None
+    out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    fp8 = cfg.kv_dtype == "e4m3"
+    torch.cuda.synchronize()
+
+    ev = {}
+
+    def step(i, timed=False):
+        g = copies[i % R]
+        if not fp8:
+            kw = {}
+            if cfg.fused_append:
+                kw = dict(q=g["q"], gamma_q=g["gamma_q"], gamma_k=g["gamma_k"],
+                          context_lens=g["context_lens"], eps=cfg.eps, rope_theta=cfg.theta)
+            _lib.paged_kv_append(g["k_new"], g["v_new"], g["k_pool"], g["v_pool"],
+                                 g["slot_mapping"], stream=stream, **kw)
+        if timed:
+            ev["d0"][i].record(stream)
+        _lib.paged_attn_decode(out if PS == 0 else None, g["q"], g["k_pool"], g["v_pool"],
+                               g["block_tables"], g["context_lens"], cfg.scale,
+                               k_scale=g.get("k_scale"), v_scale=g.get("v_scale"),
+                               partition_size=PS, part_out=ws and ws[0],
+                               part_max=ws and ws[1], part_sum=ws and ws[2], stream=stream)
+        if timed:
+            ev["d1"][i].record(stream)
+        if PS:
+            _lib.paged_attn_reduce(out, ws[0], ws[1], ws[2], g["context_lens"], PS,
+                                   stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev["d0"] = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev["d1"] = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step(i, timed=True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    dec_ms = [ev["d0"][i].elapsed_time(ev["d1"][i]) for i in range(K)]
+    dec_avg = float(np.mean(dec_ms))
+
+    kv = synth.kv_bytes(cfg, d["context_lens"])
+    tokens = int(d["context_lens"].astype(np.int64).sum())
+    value = kv / (ms * 1e-3) / 1e9
+    achieved = kv / (dec_avg * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3-kv/f16-q/f32-acc" if fp8 else "f16-kv/f32-acc",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.description,
+            "name": cfg.name,
+            "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "head_dim": cfg.D, "block_size": 16,
+            "kv_dtype": cfg.kv_dtype, "partition_size": PS,
+            "context_tokens": tokens, "mean_context": round(tokens / cfg.B, 1),
+            "step": ("decode+reduce" if fp8 else
+                     ("fused_append+decode+reduce" if cfg.fused_append else "append+decode+reduce")),
+            "rotated_copies": R,
+        },
+        "steps_per_s": round(1e3 / ms, 1),
+        "tokens_per_s": round(cfg.B * 1e3 / ms, 1),
+        "pct_hbm_peak": round(100 * value / HBM_GBPS, 2),
+        "kv_bytes_per_step": kv,
+        "decode_kernel_us": round(dec_avg * 1e3, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_GBPS, 4),
+            "traffic": None,
+            "kernel": "paged_attn_decode",
+            "algorithmic_bytes_per_launch": kv,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * pagedkv.h - batched-decode PagedAttention for AMD MI355X (gfx950).
+ *
+ * C ABI of libpagedkv.so.  Every entry point takes plain pointers and sizes;
+ * no allocation, no synchronisation and no state is kept by the library
+ * (thread-safe).  Device pointers are caller-owned HIP device memory; work
+ * is enqueued on `stream` (a hipStream_t passed as void*, NULL = the null
+ * stream) and the call returns without waiting for it.
+ *
+ * The method (page titles, sections):
+ *  - "Distributed LLM Inference Serving Platform", section 2: a sequence's
+ *    KV cache lives in fixed 16-token blocks taken from a pool; a per-
+ *    sequence block table maps logical block n (tokens 16n..16n+15) to a
+ *    physical block.  Section 5.1: each decode step writes the new token's
+ *    K/V into its physical block, then the sequence's single new query
+ *    token attends over every block in its table.
+ *  - "Roadmap: vLLM-style serving features for TornadoVM batched decode":
+ *    B independent sequences advance one token per step (Core batched
+ *    decode); block-pool KV with a per-slot block table (Serving /
+ *    scheduling); Qwen3's per-head QK-norm + split-half RoPE (Core batched
+ *    decode); a quantized FP8 KV cache (Sampling / logits).
+ *
+ * Layouts (row-major, the pages fix none):
+ *   q, out       [B][Hq][D]          fp16
+ *   k/v pool     [NB][Hkv][BS][D]    fp16, or E4M3 bytes (OCP FN format)
+ *   k/v scale    [NB][Hkv]           fp32, E4M3 only: value = e4m3(code) * scale
+ *   block_tables [B][MBS]            int32 physical block ids
+ *   context_lens [B]                 int32, valid tokens incl. this step's
+ *   slot_mapping [T]                 int64, block * BS + row; < 0 = skip
+ *   part_out     [B][Hq][P][D]       fp32 (P = max_partitions)
+ *   part_max     [B][Hq][P]          fp32
+ *   part_sum     [B][Hq][P]          fp32
+ * q head h reads kv head h / (Hq / Hkv) (contiguous GQA groups).
+ *
+ * Supported shapes: D in {64, 128}; BS == 16; Hq % Hkv == 0 with
+ * Hq / Hkv in {1, 2, 4, 8}; partition_size 0 or a positive multiple of 16
+ * no larger than 16384; MBS * BS <= 2^24.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued;
+ * a failed check returns PKV_EINVAL or PKV_EUNSUPPORTED and enqueues
+ * nothing.  A failed launch returns PKV_ELAUNCH.  Device-resident data is
+ * the caller's contract and is NOT checked: block ids < NB for the first
+ * ceil(L/16) table entries, 0 <= context_lens[b] <= MBS*16, distinct slots
+ * < NB*16.  The result never depends on pool bytes outside a sequence's
+ * first context_lens[b] rows (they may hold NaN).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,       /* null/misaligned pointer, inconsistent sizes      */
+  PKV_EUNSUPPORTED = -2, /* valid but not built: head_dim, group, block size */
+  PKV_ELAUNCH = -3       /* the HIP launch itself failed                     */
+} pkv_status;
+
+typedef enum { PKV_KV_F16 = 0, PKV_KV_E4M3 = 1 } pkv_kv_dtype;
+
+/*
+ * paged_kv_append - write this step's new K/V rows into their pool slots.
+ *
+ * "Distributed LLM Inference Serving Platform", section 5.1: K/V of new
+ * tokens go straight into the sequence's assigned physical blocks.  For
+ * token i with s = slot_mapping[i] >= 0:
+ *     k_pool[s / BS][h][s % BS][:] = k_new[i][h][:]   for every kv head h
+ * and likewise for v.  Tokens with s < 0 are skipped.
+ *
+ * Fused Qwen3 prologue ("Roadmap: vLLM-style serving features for TornadoVM
+ * batched decode", Core batched decode) when gamma_k != NULL: every q head
+ * (q_inout, rewritten in place) and every k head is first normalised,
+ *     r = x / sqrt(mean(x^2) + eps) * gamma            (over D, fp32)
+ * then rotated by split-half RoPE at pos = context_lens[i] - 1,
+ *     a = pos * rope_theta^(-2j/D)                     (angle in fp64)
+ *     y_j = r_j cos a - r_{j+D/2} sin a,  y_{j+D/2} = r_{j+D/2} cos a + r_j sin a
+ * and rounded once to fp16.  v is copied unchanged.  Without fusion
+ * (gamma_k == NULL) q_inout, gamma_q and context_lens are ignored.
+ * In the fused call q_inout [T][Hq][D] and context_lens [T] are per token
+ * (one token per sequence).
+ *
+ * k_new, v_new [T][Hkv][D] fp16 (device); k_pool, v_pool [NB][Hkv][BS][D]
+ * fp16 (device, written); slot_mapping [T] int64 (device).  All device
+ * pointers 16-byte aligned.  T == 0 is a no-op.
+ */
+int paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                    const int64_t* slot_mapping, int T, int Hkv, int D, int BS,
+                    int64_t NB, void* q_inout, int Hq, const float* gamma_q,
+                    const float* gamma_k, const int32_t* context_lens, float eps,
+                    float rope_theta, void* stream);
+
+/*
+ * paged_attn_decode - one query token per sequence attends over its paged
+ * KV ("Distributed LLM Inference Serving Platform", sections 2, 3 and 5.1;
+ * "Roadmap: vLLM-style serving features for TornadoVM batched decode",
+ * Serving / scheduling):
+ *     s_t = scale * <q[b][h], K_b[h/g][t]>,  t < L_b = context_lens[b]
+ *     out[b][h] = sum_t softmax(s)_t V_b[h/g][t]
+ * One online softmax per (sequence, kv head) is shared by the g q heads of
+ * the group.  With kv_dtype == PKV_KV_E4M3 the pools hold E4M3 codes and
+ * k_scale / v_scale [NB][Hkv] give each (block, kv head) tile's scale.
+ *
+ * partition_size == 0: single pass; out [B][Hq][D] fp16 is written
+ *   (L_b == 0 gives a zero row); the part_* pointers are ignored.
+ * partition_size  > 0: each sequence's context is cut into P_b =
+ *   ceil(L_b / partition_size) partitions of that many tokens; for each
+ *   (b, h, p < P_b) the kernel writes
+ *     part_max[b][h][p] = m_p = max_t s_t            (natural-log units)
+ *     part_sum[b][h][p] = l_p = sum_t exp(s_t - m_p)
+ *     part_out[b][h][p][:] = sum_t exp(s_t - m_p) V_t / l_p
+ *   and out is not touched (may be NULL); paged_attn_reduce combines them.
+ *   max_partitions >= ceil(MBS * BS / partition_size) is required.
+ *
+ * scale must be finite and > 0.  B == 0 is a no-op.
+ */
+int paged_attn_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, const int32_t* context_lens, int B,
+                      int Hq, int Hkv, int D, int BS, int MBS, int64_t NB, float scale,
+                      int kv_dtype, int partition_size, float* part_out, float* part_max,
+                      float* part_sum, int max_partitions, void* stream);
+
+/*
+ * paged_attn_reduce - combine split-context partitions into the output.
+ * With P_b = ceil(context_lens[b] / partition_size), M = max_{p<P_b} m_p
+ * and w_p = l_p exp(m_p - M):
+ *     out[b][h][:] = sum_p w_p part_out[b][h][p][:] / sum_p w_p   (fp16, RNE)
+ * Only p < P_b is read; L_b == 0 gives a zero row.  The summation order is
+ * fixed (p ascending), so results are bitwise reproducible.
+ */
+int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
+                      const float* part_sum, const int32_t* context_lens, int B, int Hq,
+                      int D, int partition_size, int max_partitions, void* stream);
+
+/* Bytes of part_out + part_max + part_sum for the given sizes (0 on overflow). */
+size_t paged_attn_workspace_size(int B, int Hq, int D, int max_partitions);
+
+/* Static description of a pkv_status code. */
+const char* pkv_strerror(int status);
+
+/*
+ * Host-only argument checks used by the entry points above (no HIP call;
+ * safe without a GPU).  Same arguments, same return codes.
+ */
+int pkv_validate_append(const void* k_new, const void* v_new, const void* k_pool,
+                        const void* v_pool, const int64_t* slot_mapping, int T, int Hkv,
+                        int D, int BS, int64_t NB, const void* q_inout, int Hq,
+                        const float* gamma_q, const float* gamma_k,
+                        const int32_t* context_lens, float eps, float rope_theta);
+int pkv_validate_decode(const void* out, const void* q, const void* k_pool,
+                        const void* v_pool, const float* k_scale, const float* v_scale,
+                        const int32_t* block_tables, const int32_t* context_lens, int B,
+                        int Hq, int Hkv, int D, int BS, int MBS, int64_t NB, float scale,
+                        int kv_dtype, int partition_size, const float* part_out,
+                        const float* part_max, const float* part_sum, int max_partitions);
+int pkv_validate_reduce(const void* out, const float* part_out, const float* part_max,
+                        const float* part_sum, const int32_t* context_lens, int B, int Hq,
+                        int D, int partition_size, int max_partitions);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,234 @@
+"""ctypes binding of libpagedkv.so (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, checks
+dtype/shape/contiguity, and passes raw pointers, sizes and the current HIP
+stream to the C entry point of the same name (include/pagedkv.h).  All
+arithmetic happens in the library's kernels.  If the library has not been
+built, the first call raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH = 0, -1, -2, -3
+PKV_KV_F16, PKV_KV_E4M3 = 0, 1
+BLOCK_SIZE = 16
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "paged_kv_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
+                             _F, _F, _P]),
+    "paged_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64,
+                               _F, _I, _I, _P, _P, _P, _I, _P]),
+    "paged_attn_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "paged_attn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "pkv_strerror": (ctypes.c_char_p, [_I]),
+    "pkv_validate_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
+                                 _F, _F]),
+    "pkv_validate_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64,
+                                 _F, _I, _I, _P, _P, _P, _I]),
+    "pkv_validate_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I]),
+}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status} ({strerror(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpagedkv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_208_amd.build` "
+                "(or __graft_entry__.build()) before using the GPU path")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().pkv_strerror(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype, ndim=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _raise(fn, status):
+    if status != PKV_OK:
+        raise PagedKVError(fn, status)
+
+
+def _kv_dtype(pool):
+    if pool.dtype == torch.float16:
+        return PKV_KV_F16
+    if pool.dtype == torch.uint8:
+        return PKV_KV_E4M3
+    raise TypeError("KV pools must be float16 or uint8 (E4M3 codes)")
+
+
+def paged_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, *, q=None, gamma_q=None,
+                    gamma_k=None, context_lens=None, eps=1e-6, rope_theta=1e6, stream=None):
+    """Scatter new K/V rows into the pools (optionally fused QK-norm + RoPE,
+    which also rewrites q in place)."""
+    _check(k_new, "k_new", torch.float16, 3)
+    _check(v_new, "v_new", torch.float16, 3)
+    _check(k_pool, "k_pool", torch.float16, 4)
+    _check(v_pool, "v_pool", torch.float16, 4)
+    _check(slot_mapping, "slot_mapping", torch.int64, 1)
+    T, Hkv, D = k_new.shape
+    if v_new.shape != k_new.shape or slot_mapping.shape[0] != T:
+        raise ValueError("k_new, v_new and slot_mapping disagree on T/Hkv/D")
+    NB, hkv2, BS, d2 = k_pool.shape
+    if (hkv2, d2) != (Hkv, D) or v_pool.shape != k_pool.shape:
+        raise ValueError("pool shape does not match k_new")
+    Hq = 0
+    if gamma_k is not None:
+        _check(q, "q", torch.float16, 3)
+        _check(gamma_q, "gamma_q", torch.float32, 1)
+        _check(gamma_k, "gamma_k", torch.float32, 1)
+        _check(context_lens, "context_lens", torch.int32, 1)
+        Hq = q.shape[1]
+        if q.shape[0] != T or q.shape[2] != D or gamma_q.shape[0] != D or gamma_k.shape[0] != D:
+            raise ValueError("fused append: q / gamma shapes disagree")
+        if context_lens.shape[0] != T:
+            raise ValueError("fused append: context_lens must have T entries")
+    st = lib().paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                               _ptr(slot_mapping), T, Hkv, D, BS, NB, _ptr(q), Hq,
+                               _ptr(gamma_q), _ptr(gamma_k), _ptr(context_lens), float(eps),
+                               float(rope_theta), _stream(stream))
+    _raise("paged_kv_append", st)
+
+
+def max_partitions_for(max_blocks_per_seq: int, partition_size: int) -> int:
+    if partition_size == 0:
+        return 1
+    return -(-max_blocks_per_seq * BLOCK_SIZE // partition_size)
+
+
+def alloc_partials(B, Hq, D, max_partitions, device="cuda"):
+    """(part_out, part_max, part_sum) workspace tensors."""
+    return (torch.empty((B, Hq, max_partitions, D), dtype=torch.float32, device=device),
+            torch.empty((B, Hq, max_partitions), dtype=torch.float32, device=device),
+            torch.empty((B, Hq, max_partitions), dtype=torch.float32, device=device))
+
+
+def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, *,
+                      k_scale=None, v_scale=None, partition_size=0, part_out=None,
+                      part_max=None, part_sum=None, stream=None):
+    """Decode attention over the paged KV.  partition_size == 0 writes
+    ``out``; otherwise the per-partition workspace is written."""
+    _check(q, "q", torch.float16, 3)
+    kv = _kv_dtype(k_pool)
+    _check(k_pool, "k_pool", k_pool.dtype, 4)
+    _check(v_pool, "v_pool", k_pool.dtype, 4)
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(context_lens, "context_lens", torch.int32, 1)
+    B, Hq, D = q.shape
+    NB, Hkv, BS, d2 = k_pool.shape
+    if d2 != D or v_pool.shape != k_pool.shape:
+        raise ValueError("pool shape does not match q")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens must have B rows")
+    MBS = block_tables.shape[1]
+    if kv == PKV_KV_E4M3:
+        _check(k_scale, "k_scale", torch.float32, 2)
+        _check(v_scale, "v_scale", torch.float32, 2)
+        if k_scale.shape != (NB, Hkv) or v_scale.shape != (NB, Hkv):
+            raise ValueError("scales must be [NB, Hkv]")
+    P = 1
+    if partition_size == 0:
+        _check(out, "out", torch.float16, 3)
+        if tuple(out.shape) != (B, Hq, D):
+            raise ValueError("out must be [B, Hq, D]")
+    else:
+        _check(part_out, "part_out", torch.float32, 4)
+        _check(part_max, "part_max", torch.float32, 3)
+        _check(part_sum, "part_sum", torch.float32, 3)
+        P = part_out.shape[2]
+        if (tuple(part_out.shape) != (B, Hq, P, D) or tuple(part_max.shape) != (B, Hq, P)
+                or tuple(part_sum.shape) != (B, Hq, P)):
+            raise ValueError("partial workspace shapes disagree")
+    st = lib().paged_attn_decode(_ptr(out) if partition_size == 0 else None, _ptr(q),
+                                 _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                 _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, BS,
+                                 MBS, NB, float(scale), kv, int(partition_size),
+                                 _ptr(part_out), _ptr(part_max), _ptr(part_sum), P,
+                                 _stream(stream))
+    _raise("paged_attn_decode", st)
+
+
+def paged_attn_reduce(out, part_out, part_max, part_sum, context_lens, partition_size, *,
+                      stream=None):
+    _check(out, "out", torch.float16, 3)
+    _check(part_out, "part_out", torch.float32, 4)
+    _check(part_max, "part_max", torch.float32, 3)
+    _check(part_sum, "part_sum", torch.float32, 3)
+    _check(context_lens, "context_lens", torch.int32, 1)
+    B, Hq, P, D = part_out.shape
+    if tuple(out.shape) != (B, Hq, D) or context_lens.shape[0] != B:
+        raise ValueError("out / context_lens do not match the workspace")
+    st = lib().paged_attn_reduce(_ptr(out), _ptr(part_out), _ptr(part_max), _ptr(part_sum),
+                                 _ptr(context_lens), B, Hq, D, int(partition_size), P,
+                                 _stream(stream))
+    _raise("paged_attn_reduce", st)
+
+
+def workspace_size(B, Hq, D, max_partitions) -> int:
+    return int(lib().paged_attn_workspace_size(B, Hq, D, max_partitions))
+
+
+def decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale, *, k_scale=None,
+                v_scale=None, partition_size=0, workspace=None, stream=None):
+    """Decode, followed by the reduce when partitioned (same stream)."""
+    if partition_size == 0:
+        paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                          k_scale=k_scale, v_scale=v_scale, stream=stream)
+        return
+    if workspace is None:
+        P = max_partitions_for(block_tables.shape[1], partition_size)
+        workspace = alloc_partials(q.shape[0], q.shape[1], q.shape[2], P, q.device)
+    po, pm, ps = workspace
+    paged_attn_decode(None, q, k_pool, v_pool, block_tables, context_lens, scale,
+                      k_scale=k_scale, v_scale=v_scale, partition_size=partition_size,
+                      part_out=po, part_max=pm, part_sum=ps, stream=stream)
+    paged_attn_reduce(out, po, pm, ps, context_lens, partition_size, stream=stream)

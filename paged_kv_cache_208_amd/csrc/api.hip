@@ -1,0 +1,74 @@
+// C-ABI entry points of libpagedkv.so (declared and documented in
+// include/pagedkv.h): validate on the host, then enqueue the kernels.
+#include "pagedkv.h"
+#include "kernels.h"
+#include "device.h"
+
+namespace {
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
+
+}  // namespace
+
+extern "C" int paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                               const int64_t* slot_mapping, int T, int Hkv, int D, int BS,
+                               int64_t NB, void* q_inout, int Hq, const float* gamma_q,
+                               const float* gamma_k, const int32_t* context_lens, float eps,
+                               float rope_theta, void* stream) {
+  const int st = pkv_validate_append(k_new, v_new, k_pool, v_pool, slot_mapping, T, Hkv, D, BS,
+                                     NB, q_inout, Hq, gamma_q, gamma_k, context_lens, eps,
+                                     rope_theta);
+  if (st != PKV_OK || T == 0) return st;
+  const bool fused = gamma_k != nullptr;
+  pkv::AppendArgs a{k_new, v_new, k_pool, v_pool, slot_mapping,
+                    fused ? q_inout : nullptr, fused ? gamma_q : nullptr, gamma_k,
+                    fused ? context_lens : nullptr, fused ? Hq : 0, Hkv, eps, rope_theta};
+  return launch_status(pkv::launch_append(a, T, D, fused, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int paged_attn_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, const int32_t* context_lens, int B,
+                                 int Hq, int Hkv, int D, int BS, int MBS, int64_t NB, float scale,
+                                 int kv_dtype, int partition_size, float* part_out,
+                                 float* part_max, float* part_sum, int max_partitions,
+                                 void* stream) {
+  const int st = pkv_validate_decode(out, q, k_pool, v_pool, k_scale, v_scale, block_tables,
+                                     context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale, kv_dtype,
+                                     partition_size, part_out, part_max, part_sum,
+                                     max_partitions);
+  if (st != PKV_OK || B == 0) return st;
+  const bool fp8 = kv_dtype == PKV_KV_E4M3;
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.k_scale = fp8 ? k_scale : nullptr;
+  a.v_scale = fp8 ? v_scale : nullptr;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.part_out = part_out;
+  a.part_max = part_max;
+  a.part_sum = part_sum;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.MBS = MBS;
+  a.partition_size = partition_size;
+  a.max_partitions = partition_size ? max_partitions : 1;
+  a.scale_log2 = scale * pkv::kLog2e;
+  return launch_status(
+      pkv::launch_decode(a, B, D, Hq / Hkv, fp8, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
+                                 const float* part_sum, const int32_t* context_lens, int B,
+                                 int Hq, int D, int partition_size, int max_partitions,
+                                 void* stream) {
+  const int st = pkv_validate_reduce(out, part_out, part_max, part_sum, context_lens, B, Hq, D,
+                                     partition_size, max_partitions);
+  if (st != PKV_OK || B == 0) return st;
+  pkv::ReduceArgs a{out, part_out, part_max, part_sum, context_lens,
+                    Hq, D, partition_size, max_partitions};
+  return launch_status(pkv::launch_reduce(a, B, static_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,56 @@
+// Kernel argument blocks and launchers shared by the C-ABI layer (api.hip)
+// and the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace pkv {
+
+struct DecodeArgs {
+  void* out;                  // [B][Hq][D] fp16, single pass only
+  const void* q;              // [B][Hq][D] fp16
+  const uint8_t* k_pool;      // [NB][Hkv][16][D] fp16 or E4M3
+  const uint8_t* v_pool;
+  const float* k_scale;       // [NB][Hkv], E4M3 only
+  const float* v_scale;
+  const int32_t* block_tables;  // [B][MBS]
+  const int32_t* context_lens;  // [B]
+  float* part_out;            // [B][Hq][P][D]
+  float* part_max;            // [B][Hq][P]
+  float* part_sum;            // [B][Hq][P]
+  int Hq, Hkv, MBS;
+  int partition_size;         // 0 = single pass
+  int max_partitions;         // P (partitioned) or 1
+  float scale_log2;           // softmax scale * log2(e)
+};
+
+struct ReduceArgs {
+  void* out;                  // [B][Hq][D] fp16
+  const float* part_out;
+  const float* part_max;
+  const float* part_sum;
+  const int32_t* context_lens;
+  int Hq, D, partition_size, max_partitions;
+};
+
+struct AppendArgs {
+  const void* k_new;          // [T][Hkv][D] fp16
+  const void* v_new;
+  void* k_pool;               // [NB][Hkv][16][D] fp16
+  void* v_pool;
+  const int64_t* slot_mapping;  // [T]
+  void* q;                    // [T][Hq][D] fp16, fused only (in place)
+  const float* gamma_q;       // [D], fused only
+  const float* gamma_k;
+  const int32_t* context_lens;  // [T], fused only
+  int Hq, Hkv;
+  float eps, theta;
+};
+
+// Launchers return the hipError_t of the launch.
+hipError_t launch_decode(const DecodeArgs& a, int B, int D, int group, bool fp8,
+                         hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, int B, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, int T, int D, bool fused, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,12 @@
+// Shape limits shared by the host checks and the launchers.
+#pragma once
+#include <cstdint>
+
+namespace pkv {
+constexpr int kBlockSize = 16;            // tokens per physical KV block
+constexpr int kPartitionQuantum = 16;     // partition sizes are whole blocks
+constexpr int kMaxPartition = 16384;      // tokens per split-context partition
+constexpr int64_t kMaxContext = int64_t(1) << 24;   // MBS * BS
+constexpr int64_t kMaxGrid = (int64_t(1) << 24) - 1;  // workgroups per launch (x <= 2^32 / 256)
+constexpr int64_t kMaxAppendRows = int64_t(1) << 24;
+}  // namespace pkv
