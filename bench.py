@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget for the oracle baseline")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="after timing, run plain device copies of this many MiB (a known-size "
+                        "kernel that profiler byte counters can be scaled against)")
     return p.parse_args()
 
 
@@ -199,6 +202,15 @@ def main():
     ms = start.elapsed_time(end) / K
     dec_ms = [ev["d0"][i].elapsed_time(ev["d1"][i]) for i in range(K)]
     dec_avg = float(np.mean(dec_ms))
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     kv = synth.kv_bytes(cfg, d["context_lens"])
     tokens = int(d["context_lens"].astype(np.int64).sum())

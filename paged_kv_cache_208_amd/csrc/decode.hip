@@ -9,36 +9,452 @@
 // 2): logical block n of sequence b is physical block block_tables[b][n];
 // its (block, kv head) tile of 16 token rows is contiguous in the pool
 // ([NB][Hkv][16][D] layout), 16 * D * bytes long.  The waves of a workgroup
-// take the unit's tiles round-robin.
+// take the unit's tiles round-robin, and each wave keeps the next tile's
+// loads in flight while it computes on the current one (two register
+// buffers used alternately).
 //
-// Lane mapping: a token row of one head is ROW = D * bytes long and is read
-// by LPT = ROW / 16 lanes with one 16-byte load each, so one wave load
-// covers TPI = 64 / LPT consecutive rows (a contiguous 1 KiB) and a tile
-// takes NI = 16 / TPI loads.  Each lane dots its 16 bytes of K with the
-// matching slice of the g query heads; a DPP reduction inside the LPT-lane
-// group completes the logit.  Every lane group (one token row of each wave
-// load) keeps its own running max / sum / accumulator; groups and waves are
-// merged once at the end of the unit.
-//
-// Rows past the end of the context are never fetched: the tile's buffer
+// Rows past the end of the context are never fetched: a tile's buffer
 // resource is bounded to its valid rows, loads beyond return zero, and the
 // logits of those rows are replaced by -inf before the softmax, so pad rows
 // holding anything (NaN included) cannot reach the output.
+//
+// Two tile engines compute the same thing:
+//  * MFMA (default): S^T = K Q^T with v_mfma_f32_16x16x32_f16 (16 tokens x
+//    16 head slots, the g real heads padded with zero queries), then
+//    O^T += V^T P^T with v_mfma_f32_16x16x16_f16.  The QK result layout is
+//    exactly the B-operand layout the PV product needs, so P never leaves
+//    the registers; V is regrouped into token-major quads with byte
+//    permutes.  About 50 VALU instructions per fp16 tile.
+//  * VALU: 16-byte K/V slices per lane, v_dot2 partial logits completed by
+//    DPP row reductions, fp32 FMAs for P.V.  About 430 VALU instructions
+//    per fp16 tile.
 #include "device.h"
 #include "kernels.h"
+
+// Tuning knobs (compile-time): waves per workgroup, the occupancy the
+// register allocator is asked to reach (waves per SIMD), and the order in
+// which work units are dispatched.
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+#ifndef PKV_DECODE_WAVES_PER_EU
+#define PKV_DECODE_WAVES_PER_EU 3
+#endif
+#ifndef PKV_DECODE_PARTITION_MAJOR
+#define PKV_DECODE_PARTITION_MAJOR 1
+#endif
+
+#define PKV_DECODE_BOUNDS(NW) \
+  __launch_bounds__((NW) * kWave) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, 8)))
+// the VALU engine keeps its whole g x D/4 accumulator in registers: no
+// occupancy target, so large groups do not spill
+#define PKV_DECODE_VALU_BOUNDS(NW) __launch_bounds__((NW) * kWave)
 
 namespace pkv {
 namespace {
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Shared: unit bounds, tile addressing and the cross-wave combine.
+
+struct Unit {
+  int b, kvh, p;
+  int tok_lo, tok_hi;  // token range of the unit
+  int n_lo, n_hi;      // logical block range
+  bool empty;          // partitioned and past the context: nothing to write
+};
+
+__device__ __forceinline__ Unit decode_unit(const DecodeArgs& a) {
+  Unit u;
+  int x = blockIdx.x;
+#if PKV_DECODE_PARTITION_MAJOR
+  // partition-major: every sequence's first partitions are dispatched before
+  // any sequence's later (shorter or empty) ones
+  const int bh = gridDim.x / a.max_partitions;  // B * Hkv
+  u.p = x / bh;
+  x %= bh;
+#else
+  u.p = x % a.max_partitions;
+  x /= a.max_partitions;
+#endif
+  u.kvh = x % a.Hkv;
+  u.b = x / a.Hkv;
+  const int L = a.context_lens[u.b];
+  u.tok_lo = 0;
+  u.tok_hi = L;
+  u.empty = false;
+  if (a.partition_size) {
+    u.tok_lo = u.p * a.partition_size;
+    u.empty = u.tok_lo >= L;
+    u.tok_hi = min(L, u.tok_lo + a.partition_size);
+  }
+  u.n_lo = u.tok_lo / 16;
+  u.n_hi = (u.tok_hi + 15) / 16;
+  return u;
+}
+
+// The tiles one wave visits in a unit: logical blocks n0 + NW*k, k < count.
+// Their physical block ids are read into a VGPR window (lane j holds the id
+// of tile base + j) once per chunk of up to 64 tiles and picked out with
+// readlane.  The window is filled only outside the tile loop, so the loop
+// never waits on it and the next tile's loads stay in flight while the
+// current tile is computed.
+template <int NW>
+struct TileWalk {
+  const int32_t* trow;
+  int n0, count;   // the wave's tiles
+  int base, end;   // tiles [base, end) are in the window
+  int win;
+
+  __device__ __forceinline__ void init(const int32_t* row, const Unit& u, int w) {
+    trow = row;
+    n0 = u.n_lo + w;
+    count = n0 < u.n_hi ? (u.n_hi - n0 + NW - 1) / NW : 0;
+  }
+  __device__ __forceinline__ void fill(int first) {
+    const int k = first + int(threadIdx.x & (kWave - 1));
+    base = first;
+    end = min(count, first + kWave);
+    win = k < end ? trow[n0 + NW * k] : 0;
+  }
+};
+
+// Byte offset of the wave's tile k for the unit's kv head, and its number of
+// valid rows.  Tiles outside the current window (past the chunk or the
+// wave's last tile) give 0 rows: their buffer resource has zero size and
+// nothing is read.
+template <int TILE, int NW>
+__device__ __forceinline__ int tile_base(const DecodeArgs& a, const TileWalk<NW>& walk, int k,
+                                         const Unit& u, size_t& base) {
+  int id = 0, rows = 0;
+  if (k < walk.end) {
+    id = __builtin_amdgcn_readlane(walk.win, k - walk.base);
+    rows = min(16, u.tok_hi - (walk.n0 + NW * k) * 16);
+  }
+  base = (size_t(id) * a.Hkv + u.kvh) * TILE;
+  return rows;
+}
+
+// Keeps the instruction scheduler from moving work on the current tile (and
+// so its wait for that tile's data) above the next tile's loads.
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Combine the NW waves' (m, l, acc) held in LDS and write the result.
+// m is in log2 units of the scaled logit; acc is unnormalised.
+template <int D, int G, int NW>
+__device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const Unit& u,
+                                                  float (*s_acc)[G][D], float (*s_m)[G],
+                                                  float (*s_l)[G]) {
+  const int h0 = u.kvh * G;
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+    const int j = idx / D;
+    const int d = idx % D;
+    float M = s_m[0][j];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][j]);
+    float den = 0.0f, num = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(s_m[w][j] - M);
+      den = fmaf(s_l[w][j], f, den);
+      num = fmaf(s_acc[w][j][d], f, num);
+    }
+    const size_t row = size_t(u.b) * a.Hq + h0 + j;
+    if (a.partition_size == 0) {
+      // an empty context is a zero row; anything else divides, so a NaN that
+      // reached the sums stays visible
+      static_cast<_Float16*>(a.out)[row * D + d] = (_Float16)(u.tok_hi > 0 ? num / den : 0.0f);
+    } else {
+      const size_t pr = row * a.max_partitions + u.p;
+      a.part_out[pr * D + d] = num / den;
+      if (d == 0) {
+        a.part_max[pr] = M * kLn2;
+        a.part_sum[pr] = den;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA engine.
+//
+// Lane l = 16 g + n16 (g = lane group 0..3, n16 = 0..15):
+//   K:  row n16 of the tile, 16-byte pieces 4u + g of that row
+//   QK: S^T rows are tokens, columns head slots; the lane receives tokens
+//       4g .. 4g+3 of head slot n16
+//   V:  rows 4g .. 4g+3, the D/16 dims starting at n16 * D/16
+//   PV: O^T rows are dims, columns head slots; product i covers dim
+//       (row * D/16 + i), so the lane accumulates head n16, dims
+//       (4g + r) * D/16 + i.
+
+template <int D, bool FP8>
+struct MfmaGeo {
+  static constexpr int kBytes = FP8 ? 1 : 2;
+  static constexpr int kRow = D * kBytes;       // bytes of one token row
+  static constexpr int kTile = 16 * kRow;       // bytes of a (block, kv head) tile
+  static constexpr int kPieces = kRow / 16;     // 16-byte pieces per row
+  static constexpr int kKLoads = kPieces / 4;   // K pieces per lane: 4u + lane group
+  static constexpr int kQK = D / 32;            // 16x16x32 products per tile
+  static constexpr int kPV = D / 16;            // 16x16x16 products per tile
+  static constexpr int kVBytes = kRow / 16;     // V bytes per lane per row (D/16 dims)
+  static constexpr int kVWords = kVBytes / 4;
+};
+
+template <int W>
+struct Words;
+template <>
+struct Words<1> {
+  using T = uint32_t;
+};
+template <>
+struct Words<2> {
+  using T = u32x2;
+};
+template <>
+struct Words<4> {
+  using T = u32x4;
+};
+
+template <int W>
+__device__ __forceinline__ typename Words<W>::T buffer_load_words(__amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (W == 4) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  else if constexpr (W == 2) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+template <int W>
+__device__ __forceinline__ uint32_t word(const typename Words<W>::T& v, int k) {
+  if constexpr (W == 1) return v;
+  else return v[k];
+}
+
+template <int D, bool FP8>
+struct MTile {
+  using Geo = MfmaGeo<D, FP8>;
+  u32x4 k[Geo::kKLoads];
+  typename Words<Geo::kVWords>::T v[4];
+  float ks, vs;
+  int rows;
+};
+
+template <int D, bool FP8, int NW>
+__device__ __forceinline__ void load_mtile(MTile<D, FP8>& t, const DecodeArgs& a, const TileWalk<NW>& walk,
+                                           int k, const Unit& u, int k_off, int v_off) {
+  using Geo = MfmaGeo<D, FP8>;
+  size_t base;
+  t.rows = tile_base<Geo::kTile, NW>(a, walk, k, u, base);
+  const int nbytes = t.rows * Geo::kRow;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_pool + base, nbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_pool + base, nbytes);
+#pragma unroll
+  for (int i = 0; i < Geo::kKLoads; ++i) t.k[i] = buffer_load16(rk, k_off + i * 64);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t.v[j] = buffer_load_words<Geo::kVWords>(rv, v_off + j * Geo::kRow);
+  t.ks = t.vs = 1.0f;
+  if constexpr (FP8) {
+    if (t.rows > 0) {
+      const size_t s = base / Geo::kTile;  // == block id * Hkv + kv head
+      t.ks = a.k_scale[s];
+      t.vs = a.v_scale[s];
+    }
+  }
+}
+
+// A operand (K rows) of QK product c: 8 dims per lane.
+template <int D, bool FP8>
+__device__ __forceinline__ half8_t k_operand(const MTile<D, FP8>& t, int c) {
+  if constexpr (!FP8) {
+    return __builtin_bit_cast(half8_t, t.k[c]);
+  } else {
+    const u32x4& p = t.k[c / 2];
+    const uint32_t w0 = p[2 * (c % 2)], w1 = p[2 * (c % 2) + 1];
+    const half2_t a = e4m3x2_to_half2<false>(w0), b = e4m3x2_to_half2<true>(w0);
+    const half2_t e = e4m3x2_to_half2<false>(w1), f = e4m3x2_to_half2<true>(w1);
+    return half8_t{a.x, a.y, b.x, b.y, e.x, e.y, f.x, f.y};
+  }
+}
+
+// First of the 8 dims that QK product c takes from lane group g (the K
+// operand above and the q operand must agree on it).
+template <bool FP8>
+__device__ __forceinline__ int qk_dim0(int c, int g) {
+  if constexpr (!FP8) return 8 * (4 * c + g);
+  else return 16 * (4 * (c / 2) + g) + 8 * (c % 2);
+}
+
+// A operand (V^T) of PV product i: element i of the lane's V slice in each
+// of its four rows 4g + 0..3.
+template <int D, bool FP8>
+__device__ __forceinline__ half4_t v_operand(const MTile<D, FP8>& t, int i) {
+  using Geo = MfmaGeo<D, FP8>;
+  if constexpr (!FP8) {
+    const int wi = i / 2;
+    const uint32_t x0 = word<Geo::kVWords>(t.v[0], wi), x1 = word<Geo::kVWords>(t.v[1], wi);
+    const uint32_t x2 = word<Geo::kVWords>(t.v[2], wi), x3 = word<Geo::kVWords>(t.v[3], wi);
+    uint32_t lo, hi;
+    if (i % 2 == 0) {
+      lo = (x0 & 0xFFFFu) | (x1 << 16);
+      hi = (x2 & 0xFFFFu) | (x3 << 16);
+    } else {
+      lo = (x0 >> 16) | (x1 & 0xFFFF0000u);
+      hi = (x2 >> 16) | (x3 & 0xFFFF0000u);
+    }
+    const u32x2 r = {lo, hi};
+    return __builtin_bit_cast(half4_t, r);
+  } else {
+    const int wi = i / 4, sh = 8 * (i % 4);
+    const uint32_t b0 = (word<Geo::kVWords>(t.v[0], wi) >> sh) & 0xFFu;
+    const uint32_t b1 = (word<Geo::kVWords>(t.v[1], wi) >> sh) & 0xFFu;
+    const uint32_t b2 = (word<Geo::kVWords>(t.v[2], wi) >> sh) & 0xFFu;
+    const uint32_t b3 = (word<Geo::kVWords>(t.v[3], wi) >> sh) & 0xFFu;
+    const uint32_t w = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    const half2_t a = e4m3x2_to_half2<false>(w), c = e4m3x2_to_half2<true>(w);
+    return half4_t{a.x, a.y, c.x, c.y};
+  }
+}
+
+template <int D, bool FP8>
+struct MState {
+  float m;  // running max of head slot n16, log2 units of the scaled logit
+  float l;  // this lane's share of the exp-sum (its 4 tokens per tile)
+  float4_t acc[MfmaGeo<D, FP8>::kPV];
+};
+
+template <int D, bool FP8>
+__device__ __forceinline__ void mfma_tile(MState<D, FP8>& st, const MTile<D, FP8>& t,
+                                          const half8_t* qop, float scale_log2, int g) {
+  using Geo = MfmaGeo<D, FP8>;
+  float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < Geo::kQK; ++c)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<D, FP8>(t, c), qop[c], s, 0, 0, 0);
+  const float cs = scale_log2 * t.ks;
+  float tm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s[r] = (4 * g + r) < t.rows ? s[r] : -INFINITY;
+    tm = fmaxf(tm, s[r]);
+  }
+  // the head's 16 tokens sit in lanes n16, n16+16, n16+32, n16+48
+  tm = fmaxf(tm, __shfl_xor(tm, 16));
+  tm = fmaxf(tm, __shfl_xor(tm, 32));
+  const float mn = fmaxf(st.m, tm * cs);
+  const float alpha = fast_exp2(st.m - mn);
+  st.m = mn;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // skip the rescale when no max moved
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < Geo::kPV; ++i) st.acc[i] *= alpha;
+  }
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    p[r] = fast_exp2(fmaf(s[r], cs, -mn));
+    st.l += p[r];
+  }
+  const half4_t pv = {(_Float16)(p[0] * t.vs), (_Float16)(p[1] * t.vs), (_Float16)(p[2] * t.vs),
+                      (_Float16)(p[3] * t.vs)};
+#pragma unroll
+  for (int i = 0; i < Geo::kPV; ++i)
+    st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v_operand<D, FP8>(t, i), pv, st.acc[i], 0, 0, 0);
+}
+
+template <int D, int G, bool FP8, int NW>
+__global__ PKV_DECODE_BOUNDS(NW) void decode_mfma_kernel(DecodeArgs a) {
+  using Geo = MfmaGeo<D, FP8>;
+  static_assert(G <= 16, "head slots of one 16-wide product");
+  const Unit u = decode_unit(a);
+  if (u.empty) return;  // whole workgroup
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = lane / 16;
+  const int n16 = lane % 16;
+
+  // B operand of the QK products: q of head slot n16 (zero past the group)
+  half8_t qop[Geo::kQK];
+  {
+    const _Float16* qh =
+        static_cast<const _Float16*>(a.q) + (size_t(u.b) * a.Hq + u.kvh * G + min(n16, G - 1)) * D;
+#pragma unroll
+    for (int c = 0; c < Geo::kQK; ++c) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qh + qk_dim0<FP8>(c, g));
+      qop[c] = n16 < G ? __builtin_bit_cast(half8_t, x) : half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  MState<D, FP8> st;
+  st.m = -FLT_MAX;
+  st.l = 0.0f;
+#pragma unroll
+  for (int i = 0; i < Geo::kPV; ++i) st.acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  TileWalk<NW> walk;
+  walk.init(a.block_tables + size_t(u.b) * a.MBS, u, w);
+  const int k_off = n16 * Geo::kRow + g * 16;
+  const int v_off = (4 * g) * Geo::kRow + n16 * Geo::kVBytes;
+
+  MTile<D, FP8> ta, tb;
+  for (int c0 = 0; c0 < walk.count; c0 += kWave) {
+    walk.fill(c0);
+    load_mtile<D, FP8, NW>(ta, a, walk, c0, u, k_off, v_off);
+    for (int k = c0; k < walk.end;) {
+      load_mtile<D, FP8, NW>(tb, a, walk, k + 1, u, k_off, v_off);
+      issue_fence();
+      mfma_tile<D, FP8>(st, ta, qop, a.scale_log2, g);
+      if (++k >= walk.end) break;
+      load_mtile<D, FP8, NW>(ta, a, walk, k + 1, u, k_off, v_off);
+      issue_fence();
+      mfma_tile<D, FP8>(st, tb, qop, a.scale_log2, g);
+      ++k;
+    }
+  }
+
+  // the four lane groups of a head hold disjoint tokens: add their sums
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+
+  __shared__ float s_acc[NW][G][D];
+  __shared__ float s_m[NW][G];
+  __shared__ float s_l[NW][G];
+  if (n16 < G) {
+#pragma unroll
+    for (int i = 0; i < Geo::kPV; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_acc[w][n16][(4 * g + r) * (D / 16) + i] = st.acc[i][r];
+    if (g == 0) {
+      s_m[w][n16] = st.m;
+      s_l[w][n16] = st.l;
+    }
+  }
+  __syncthreads();
+  combine_and_store<D, G, NW>(a, u, s_acc, s_m, s_l);
+}
+
+// ---------------------------------------------------------------------------
+// VALU engine.
+//
+// A token row of one head is ROW = D * bytes long and is read by
+// LPT = ROW / 16 lanes with one 16-byte load each, so one wave load covers
+// TPI = 64 / LPT consecutive rows (a contiguous 1 KiB) and a tile takes
+// NI = 16 / TPI loads.  Each lane dots its 16 bytes of K with the matching
+// slice of the g query heads; a DPP reduction inside the LPT-lane group
+// completes the logit.  Every lane group keeps its own running max / sum /
+// accumulator; groups and waves are merged once at the end of the unit.
+
 template <int D, bool FP8>
 struct Geometry {
   static constexpr int kBytes = FP8 ? 1 : 2;
-  static constexpr int kRow = D * kBytes;     // bytes of one token row
-  static constexpr int kLpt = kRow / 16;      // lanes per token row
-  static constexpr int kTpi = kWave / kLpt;   // token rows per wave load
-  static constexpr int kNi = 16 / kTpi;       // wave loads per tile
-  static constexpr int kEpl = 16 / kBytes;    // elements per lane
-  static constexpr int kTile = 16 * kRow;     // bytes per (block, kv head) tile
+  static constexpr int kRow = D * kBytes;
+  static constexpr int kLpt = kRow / 16;
+  static constexpr int kTpi = kWave / kLpt;
+  static constexpr int kNi = 16 / kTpi;
+  static constexpr int kEpl = 16 / kBytes;
+  static constexpr int kTile = 16 * kRow;
   static_assert(kLpt >= 4 && kLpt <= 16, "row must span 4..16 lanes");
 };
 
@@ -47,42 +463,33 @@ struct TileRegs {
   using Geo = Geometry<D, FP8>;
   u32x4 k[Geo::kNi];
   u32x4 v[Geo::kNi];
-  float ks, vs;  // E4M3 tile scales (1 for fp16)
-  int rows;      // valid token rows in the tile (0 = past the unit)
+  float ks, vs;
+  int rows;
 };
 
-template <int D, bool FP8>
-__device__ __forceinline__ void load_tile(TileRegs<D, FP8>& t, const DecodeArgs& a,
-                                          const int32_t* trow, int n, int n_hi, int tok_hi,
-                                          int kvh, int lane_off) {
+template <int D, bool FP8, int NW>
+__device__ __forceinline__ void load_tile(TileRegs<D, FP8>& t, const DecodeArgs& a, const TileWalk<NW>& walk,
+                                          int k, const Unit& u, int lane_off) {
   using Geo = Geometry<D, FP8>;
-  int id = 0;
-  t.rows = 0;
-  if (n < n_hi) {
-    id = __builtin_amdgcn_readfirstlane(trow[n]);
-    t.rows = min(16, tok_hi - n * 16);
-  }
-  const size_t tile = (size_t(id) * a.Hkv + kvh) * Geo::kTile;
+  size_t base;
+  t.rows = tile_base<Geo::kTile, NW>(a, walk, k, u, base);
   const int nbytes = t.rows * Geo::kRow;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_pool + tile, nbytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_pool + tile, nbytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_pool + base, nbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_pool + base, nbytes);
 #pragma unroll
   for (int i = 0; i < Geo::kNi; ++i) t.k[i] = buffer_load16(rk, lane_off + i * Geo::kTpi * Geo::kRow);
 #pragma unroll
   for (int i = 0; i < Geo::kNi; ++i) t.v[i] = buffer_load16(rv, lane_off + i * Geo::kTpi * Geo::kRow);
+  t.ks = t.vs = 1.0f;
   if constexpr (FP8) {
-    t.ks = 1.0f;
-    t.vs = 1.0f;
-    if (n < n_hi) {
-      t.ks = a.k_scale[size_t(id) * a.Hkv + kvh];
-      t.vs = a.v_scale[size_t(id) * a.Hkv + kvh];
+    if (t.rows > 0) {
+      const size_t s = base / Geo::kTile;
+      t.ks = a.k_scale[s];
+      t.vs = a.v_scale[s];
     }
-  } else {
-    t.ks = t.vs = 1.0f;
   }
 }
 
-// Partial dot of one lane's 16 bytes of K with one q head's matching slice.
 template <int D, bool FP8>
 __device__ __forceinline__ float lane_dot(const u32x4& kw, const half2_t* qh) {
   float s = 0.0f;
@@ -102,7 +509,6 @@ __device__ __forceinline__ float lane_dot(const u32x4& kw, const half2_t* qh) {
   return s;
 }
 
-// The lane's 16 bytes of V as EPL floats.
 template <bool FP8>
 __device__ __forceinline__ void lane_values(const u32x4& vw, float* out) {
   const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
@@ -126,36 +532,71 @@ __device__ __forceinline__ void lane_values(const u32x4& vw, float* out) {
   }
 }
 
-template <int D, int G, bool FP8, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_kernel(DecodeArgs a) {
+template <int D, int G, bool FP8>
+struct VState {
+  static constexpr int EPL = Geometry<D, FP8>::kEpl;
+  float m[G], l[G], acc[G][EPL];
+};
+
+template <int D, int G, bool FP8>
+__device__ __forceinline__ void valu_tile(VState<D, G, FP8>& st, const TileRegs<D, FP8>& t,
+                                          const half2_t (*qv)[Geometry<D, FP8>::kEpl / 2],
+                                          float scale_log2, int r) {
   using Geo = Geometry<D, FP8>;
   constexpr int LPT = Geo::kLpt, TPI = Geo::kTpi, NI = Geo::kNi, EPL = Geo::kEpl;
+  float s[NI][G];  // raw logits of this lane group's rows
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const bool valid = (i * TPI + r) < t.rows;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float d = group_sum<LPT>(lane_dot<D, FP8>(t.k[i], qv[j]));
+      s[i][j] = valid ? d : -INFINITY;
+    }
+  }
+  float vals[NI][EPL];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) lane_values<FP8>(t.v[i], vals[i]);
+  const float cs = scale_log2 * t.ks;
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float tmax = s[0][j];
+#pragma unroll
+    for (int i = 1; i < NI; ++i) tmax = fmaxf(tmax, s[i][j]);
+    const float mn = fmaxf(st.m[j], tmax * cs);
+    const float alpha = fast_exp2(st.m[j] - mn);
+    st.m[j] = mn;
+    st.l[j] *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) st.acc[j][e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float pij = fast_exp2(fmaf(s[i][j], cs, -mn));
+      st.l[j] += pij;
+      const float pv = pij * t.vs;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) st.acc[j][e] = fmaf(pv, vals[i][e], st.acc[j][e]);
+    }
+  }
+}
+
+template <int D, int G, bool FP8, int NW>
+__global__ PKV_DECODE_VALU_BOUNDS(NW) void decode_valu_kernel(DecodeArgs a) {
+  using Geo = Geometry<D, FP8>;
+  constexpr int LPT = Geo::kLpt, EPL = Geo::kEpl;
+  const Unit u = decode_unit(a);
+  if (u.empty) return;  // whole workgroup
 
   const int lane = threadIdx.x & (kWave - 1);
   // wave index as a scalar: keeps the tile walk, block ids and buffer
   // resources in SGPRs
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int r = lane / LPT;  // token row within a wave load
-  const int c = lane % LPT;  // 16-byte column within the row
+  const int r = lane / LPT;
+  const int c = lane % LPT;
 
-  int unit = blockIdx.x;
-  const int p = unit % a.max_partitions;
-  unit /= a.max_partitions;
-  const int kvh = unit % a.Hkv;
-  const int b = unit / a.Hkv;
-
-  const int L = a.context_lens[b];
-  int tok_lo = 0, tok_hi = L;
-  if (a.partition_size) {
-    tok_lo = p * a.partition_size;
-    if (tok_lo >= L) return;  // whole workgroup: partition past the context
-    tok_hi = min(L, tok_lo + a.partition_size);
-  }
-
-  // q slice of every head of the group: elements [c*EPL, c*EPL + EPL)
-  half2_t qv[G][EPL / 2];
+  half2_t qv[G][EPL / 2];  // q slice of every head: elements [c*EPL, c*EPL + EPL)
   {
-    const _Float16* qb = static_cast<const _Float16*>(a.q) + (size_t(b) * a.Hq + kvh * G) * D + c * EPL;
+    const _Float16* qb = static_cast<const _Float16*>(a.q) + (size_t(u.b) * a.Hq + u.kvh * G) * D + c * EPL;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
 #pragma unroll
@@ -169,85 +610,51 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  float m[G], l[G], acc[G][EPL];
+  VState<D, G, FP8> st;
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    m[j] = -FLT_MAX;
-    l[j] = 0.0f;
+    st.m[j] = -FLT_MAX;
+    st.l[j] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[j][e] = 0.0f;
+    for (int e = 0; e < EPL; ++e) st.acc[j][e] = 0.0f;
   }
 
-  const int n_lo = tok_lo / 16;
-  const int n_hi = (tok_hi + 15) / 16;
-  const int32_t* trow = a.block_tables + size_t(b) * a.MBS;
+  TileWalk<NW> walk;
+  walk.init(a.block_tables + size_t(u.b) * a.MBS, u, w);
   const int lane_off = r * Geo::kRow + c * 16;
-
-  TileRegs<D, FP8> cur;
-  int n = n_lo + w;
-  load_tile<D, FP8>(cur, a, trow, n, n_hi, tok_hi, kvh, lane_off);
-  for (; n < n_hi; n += NW) {
-    TileRegs<D, FP8> nxt;
-    load_tile<D, FP8>(nxt, a, trow, n + NW, n_hi, tok_hi, kvh, lane_off);
-
-    // logits of the NI rows this lane group holds, for every head
-    float s[NI][G];
-    const float cs = a.scale_log2 * cur.ks;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const bool valid = (i * TPI + r) < cur.rows;
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const float d = group_sum<LPT>(lane_dot<D, FP8>(cur.k[i], qv[j]));
-        s[i][j] = valid ? d * cs : -INFINITY;
-      }
+  TileRegs<D, FP8> ta, tb;
+  for (int c0 = 0; c0 < walk.count; c0 += kWave) {
+    walk.fill(c0);
+    load_tile<D, FP8, NW>(ta, a, walk, c0, u, lane_off);
+    for (int k = c0; k < walk.end;) {
+      load_tile<D, FP8, NW>(tb, a, walk, k + 1, u, lane_off);
+      issue_fence();
+      valu_tile<D, G, FP8>(st, ta, qv, a.scale_log2, r);
+      if (++k >= walk.end) break;
+      load_tile<D, FP8, NW>(ta, a, walk, k + 1, u, lane_off);
+      issue_fence();
+      valu_tile<D, G, FP8>(st, tb, qv, a.scale_log2, r);
+      ++k;
     }
-
-    float vals[NI][EPL];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) lane_values<FP8>(cur.v[i], vals[i]);
-
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float tmax = s[0][j];
-#pragma unroll
-      for (int i = 1; i < NI; ++i) tmax = fmaxf(tmax, s[i][j]);
-      const float mn = fmaxf(m[j], tmax);
-      const float alpha = fast_exp2(m[j] - mn);
-      m[j] = mn;
-      l[j] *= alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float pij = fast_exp2(s[i][j] - mn);
-        l[j] += pij;
-        const float pv = pij * cur.vs;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(pv, vals[i][e], acc[j][e]);
-      }
-    }
-    cur = nxt;
   }
 
-  // merge the TPI row groups of the wave (lanes with the same column c)
+  // merge the row groups of the wave (lanes with the same column c)
 #pragma unroll
   for (int off = LPT; off < kWave; off <<= 1) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const float mo = __shfl_xor(m[j], off);
-      const float lo = __shfl_xor(l[j], off);
-      const float mn = fmaxf(m[j], mo);
-      const float fa = fast_exp2(m[j] - mn);
+      const float mo = __shfl_xor(st.m[j], off);
+      const float lo = __shfl_xor(st.l[j], off);
+      const float mn = fmaxf(st.m[j], mo);
+      const float fa = fast_exp2(st.m[j] - mn);
       const float fb = fast_exp2(mo - mn);
-      l[j] = l[j] * fa + lo * fb;
+      st.l[j] = st.l[j] * fa + lo * fb;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[j][e] = acc[j][e] * fa + __shfl_xor(acc[j][e], off) * fb;
-      m[j] = mn;
+      for (int e = 0; e < EPL; ++e) st.acc[j][e] = st.acc[j][e] * fa + __shfl_xor(st.acc[j][e], off) * fb;
+      st.m[j] = mn;
     }
   }
 
-  // merge the waves through LDS
   __shared__ float s_acc[NW][G][D];
   __shared__ float s_m[NW][G];
   __shared__ float s_l[NW][G];
@@ -255,62 +662,42 @@ __global__ __launch_bounds__(NW * kWave) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[w][j][c * EPL + e] = acc[j][e];
+      for (int e = 0; e < EPL; ++e) s_acc[w][j][c * EPL + e] = st.acc[j][e];
       if (c == 0) {
-        s_m[w][j] = m[j];
-        s_l[w][j] = l[j];
+        s_m[w][j] = st.m[j];
+        s_l[w][j] = st.l[j];
       }
     }
   }
   __syncthreads();
-
-  const int h0 = kvh * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
-    const int j = idx / D;
-    const int d = idx % D;
-    float M = s_m[0][j];
-#pragma unroll
-    for (int u = 1; u < NW; ++u) M = fmaxf(M, s_m[u][j]);
-    float den = 0.0f, num = 0.0f;
-#pragma unroll
-    for (int u = 0; u < NW; ++u) {
-      const float f = fast_exp2(s_m[u][j] - M);
-      den = fmaf(s_l[u][j], f, den);
-      num = fmaf(s_acc[u][j][d], f, num);
-    }
-    const size_t row = size_t(b) * a.Hq + h0 + j;
-    if (a.partition_size == 0) {
-      // an empty context is a zero row; anything else divides, so a NaN that
-      // reached the sums stays visible
-      static_cast<_Float16*>(a.out)[row * D + d] = (_Float16)(tok_hi > 0 ? num / den : 0.0f);
-    } else {
-      const size_t pr = row * a.max_partitions + p;
-      a.part_out[pr * D + d] = num / den;
-      if (d == 0) {
-        a.part_max[pr] = M * kLn2;
-        a.part_sum[pr] = den;
-      }
-    }
-  }
+  combine_and_store<D, G, NW>(a, u, s_acc, s_m, s_l);
 }
 
-constexpr int kWavesPerGroup = 4;
+// ---------------------------------------------------------------------------
+// Dispatch.
+
+constexpr int kWavesPerGroup = PKV_DECODE_WAVES;
 
 template <int D, int G, bool FP8>
-hipError_t launch_typed(const DecodeArgs& a, int B, hipStream_t stream) {
-  const int64_t units = int64_t(B) * a.Hkv * a.max_partitions;
-  hipLaunchKernelGGL((decode_kernel<D, G, FP8, kWavesPerGroup>), dim3(unsigned(units)),
-                     dim3(kWavesPerGroup * kWave), 0, stream, a);
+hipError_t launch_typed(const DecodeArgs& a, int B, DecodeEngine engine, hipStream_t stream) {
+  const unsigned units = unsigned(int64_t(B) * a.Hkv * a.max_partitions);
+  if (engine == DecodeEngine::kValu)
+    hipLaunchKernelGGL((decode_valu_kernel<D, G, FP8, kWavesPerGroup>), dim3(units),
+                       dim3(kWavesPerGroup * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, FP8, kWavesPerGroup>), dim3(units),
+                       dim3(kWavesPerGroup * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, bool FP8>
-hipError_t launch_group(const DecodeArgs& a, int B, int group, hipStream_t stream) {
+hipError_t launch_group(const DecodeArgs& a, int B, int group, DecodeEngine engine,
+                        hipStream_t stream) {
   switch (group) {
-    case 1: return launch_typed<D, 1, FP8>(a, B, stream);
-    case 2: return launch_typed<D, 2, FP8>(a, B, stream);
-    case 4: return launch_typed<D, 4, FP8>(a, B, stream);
-    case 8: return launch_typed<D, 8, FP8>(a, B, stream);
+    case 1: return launch_typed<D, 1, FP8>(a, B, engine, stream);
+    case 2: return launch_typed<D, 2, FP8>(a, B, engine, stream);
+    case 4: return launch_typed<D, 4, FP8>(a, B, engine, stream);
+    case 8: return launch_typed<D, 8, FP8>(a, B, engine, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -318,11 +705,11 @@ hipError_t launch_group(const DecodeArgs& a, int B, int group, hipStream_t strea
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, int group, bool fp8,
-                         hipStream_t stream) {
-  if (D == 128) return fp8 ? launch_group<128, true>(a, B, group, stream)
-                           : launch_group<128, false>(a, B, group, stream);
-  if (D == 64) return fp8 ? launch_group<64, true>(a, B, group, stream)
-                          : launch_group<64, false>(a, B, group, stream);
+                         DecodeEngine engine, hipStream_t stream) {
+  if (D == 128) return fp8 ? launch_group<128, true>(a, B, group, engine, stream)
+                           : launch_group<128, false>(a, B, group, engine, stream);
+  if (D == 64) return fp8 ? launch_group<64, true>(a, B, group, engine, stream)
+                          : launch_group<64, false>(a, B, group, engine, stream);
   return hipErrorInvalidValue;
 }
 

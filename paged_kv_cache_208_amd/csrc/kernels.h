@@ -47,9 +47,12 @@ struct AppendArgs {
   float eps, theta;
 };
 
+// Tile engine of the decode kernel (same result, different instruction mix).
+enum class DecodeEngine { kMfma, kValu };
+
 // Launchers return the hipError_t of the launch.
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, int group, bool fp8,
-                         hipStream_t stream);
+                         DecodeEngine engine, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int B, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int T, int D, bool fused, hipStream_t stream);
 
