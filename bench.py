@@ -2,11 +2,14 @@
 """Batched-decode PagedAttention benchmark on one MI355X.
 
 One step = one decode step of one attention layer over a synthetic batch:
-  * fp16 configs: paged_kv_append (this step's K/V rows into their slots)
-    -> paged_attn_decode (split-context partitions) -> paged_attn_reduce
+  * fp16 configs: this step's K/V row of every sequence is written to its
+    slot, then each query attends over its paged KV in split-context
+    partitions, which are combined into the output
   * fused config (c4): the append also applies QK-RMSNorm + RoPE to q and k
-  * E4M3 config (c5): decode over FP8 KV -> reduce
-all on one HIP stream.  Inputs are resident in HBM before timing starts;
+  * E4M3 config (c5): attention over FP8 KV + combine
+By default the step is one launch of paged_decode_step; --unfused times the
+same work as paged_kv_append -> paged_attn_decode -> paged_attn_reduce on
+one HIP stream.  Inputs are resident in HBM before timing starts;
 R rotated copies of the pools, tables and q (>= 1 GiB touched between
 reuses) keep the 256 MB last-level cache from serving the KV.
 
@@ -44,6 +47,8 @@ def parse():
     p.add_argument("--partition-size", type=int, default=None)
     p.add_argument("--rotate", type=int, default=None, help="copies of the inputs (default: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--unfused", action="store_true",
+                   help="time append, decode and reduce as three launches")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget for the oracle baseline")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -157,14 +162,14 @@ def main():
     PS = cfg.partition_size
     P = _lib.max_partitions_for(cfg.mbs, PS)
     ws = _lib.alloc_partials(B, Hq, D, P, dev) if PS else None
+    step_ws = _lib.alloc_step_workspace(B, Hq, cfg.Hkv, D, P, dev) if PS else None
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     fp8 = cfg.kv_dtype == "e4m3"
     torch.cuda.synchronize()
 
     ev = {}
 
-    def step(i, timed=False):
-        g = copies[i % R]
+    def step_unfused(g, i, timed):
         if not fp8:
             kw = {}
             if cfg.fused_append:
@@ -184,6 +189,26 @@ def main():
         if PS:
             _lib.paged_attn_reduce(out, ws[0], ws[1], ws[2], g["context_lens"], PS,
                                    stream=stream)
+
+    def step_fused(g, i, timed):
+        kw = {}
+        if not fp8:
+            kw = dict(k_new=g["k_new"], v_new=g["v_new"])
+            if cfg.fused_append:
+                kw.update(gamma_q=g["gamma_q"], gamma_k=g["gamma_k"], eps=cfg.eps,
+                          rope_theta=cfg.theta)
+        if timed:
+            ev["d0"][i].record(stream)
+        _lib.paged_decode_step(out, g["q"], g["k_pool"], g["v_pool"], g["block_tables"],
+                               g["context_lens"], cfg.scale, k_scale=g.get("k_scale"),
+                               v_scale=g.get("v_scale"), partition_size=PS, workspace=step_ws,
+                               stream=stream, **kw)
+        if timed:
+            ev["d1"][i].record(stream)
+
+    def step(i, timed=False):
+        g = copies[i % R]
+        (step_unfused if args.unfused else step_fused)(g, i, timed)
 
     for i in range(args.warmup):
         step(i)
@@ -235,8 +260,10 @@ def main():
             "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "head_dim": cfg.D, "block_size": 16,
             "kv_dtype": cfg.kv_dtype, "partition_size": PS,
             "context_tokens": tokens, "mean_context": round(tokens / cfg.B, 1),
-            "step": ("decode+reduce" if fp8 else
-                     ("fused_append+decode+reduce" if cfg.fused_append else "append+decode+reduce")),
+            "step": ("attend+combine" if fp8 else
+                     ("qknorm_rope+append+attend+combine" if cfg.fused_append
+                      else "append+attend+combine")),
+            "launches_per_step": (3 if not fp8 else 2) if args.unfused and PS else 1,
             "rotated_copies": R,
         },
         "steps_per_s": round(1e3 / ms, 1),
@@ -251,7 +278,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_GBPS, 4),
             "traffic": None,
-            "kernel": "paged_attn_decode",
+            "kernel": "paged_attn_decode" if args.unfused else "paged_decode_step",
             "algorithmic_bytes_per_launch": kv,
         },
         "cpu_baseline": cpu,

@@ -137,6 +137,41 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
                       const float* part_sum, const int32_t* context_lens, int B, int Hq,
                       int D, int partition_size, int max_partitions, void* stream);
 
+/*
+ * paged_decode_step - one whole decode step in one launch: the three calls
+ * above fused, for the common case where each sequence's new token is its
+ * last one ("Distributed LLM Inference Serving Platform", section 5.1: write
+ * the new token's K/V into its block, then attend over the block table).
+ * For every sequence b with L_b = context_lens[b] >= 1:
+ *  1. if k_new != NULL, k_new[b] and v_new[b] ([B][Hkv][D] fp16) become token
+ *     L_b - 1: they are written to block block_tables[b][(L_b-1)/BS], row
+ *     (L_b-1) % BS, of every kv head (the slot paged_kv_append would be
+ *     given).  With gamma_k != NULL the Qwen3 QK-norm + split-half RoPE at
+ *     pos = L_b - 1 is first applied to the new k and to q, which is
+ *     rewritten in place, exactly as paged_kv_append does;
+ *  2. q attends over the sequence's paged KV as in paged_attn_decode;
+ *  3. with partition_size > 0, the last workgroup to finish for each
+ *     (sequence, kv head) combines its partitions as paged_attn_reduce does,
+ *     so out [B][Hq][D] fp16 is complete when the launch is.
+ * counters: [B][Hkv] uint32 device memory, all zero before the first call;
+ *   each call leaves them zero again.  Calls sharing counters, partials or
+ *   pools must not run concurrently.  part_* are scratch as for
+ *   paged_attn_decode (contents undefined afterwards).
+ * partition_size 0: single pass; counters and part_* are not used.
+ * partition_size > 0: at most 64 partitions per sequence
+ *   (ceil(MBS * BS / partition_size) <= 64), else PKV_EUNSUPPORTED.
+ * kv_dtype PKV_KV_E4M3: attend + combine only (k_new must be NULL).
+ * L_b == 0: zero output row, nothing written to the pools, q untouched.
+ * Errors and shape limits as for paged_attn_decode and paged_kv_append.
+ */
+int paged_decode_step(void* out, void* q, const void* k_new, const void* v_new, void* k_pool,
+                      void* v_pool, const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, const int32_t* context_lens, int B, int Hq,
+                      int Hkv, int D, int BS, int MBS, int64_t NB, float scale, int kv_dtype,
+                      int partition_size, const float* gamma_q, const float* gamma_k, float eps,
+                      float rope_theta, float* part_out, float* part_max, float* part_sum,
+                      uint32_t* counters, int max_partitions, void* stream);
+
 /* Bytes of part_out + part_max + part_sum for the given sizes (0 on overflow). */
 size_t paged_attn_workspace_size(int B, int Hq, int D, int max_partitions);
 
@@ -158,6 +193,14 @@ int pkv_validate_decode(const void* out, const void* q, const void* k_pool,
                         int Hq, int Hkv, int D, int BS, int MBS, int64_t NB, float scale,
                         int kv_dtype, int partition_size, const float* part_out,
                         const float* part_max, const float* part_sum, int max_partitions);
+int pkv_validate_step(const void* out, const void* q, const void* k_new, const void* v_new,
+                      const void* k_pool, const void* v_pool, const float* k_scale,
+                      const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
+                      int MBS, int64_t NB, float scale, int kv_dtype, int partition_size,
+                      const float* gamma_q, const float* gamma_k, float eps, float rope_theta,
+                      const float* part_out, const float* part_max, const float* part_sum,
+                      const uint32_t* counters, int max_partitions);
 int pkv_validate_reduce(const void* out, const float* part_out, const float* part_max,
                         const float* part_sum, const int32_t* context_lens, int B, int Hq,
                         int D, int partition_size, int max_partitions);

@@ -35,6 +35,8 @@ _SIGNATURES = {
     "paged_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64,
                                _F, _I, _I, _P, _P, _P, _I, _P]),
     "paged_attn_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "paged_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                               _I64, _F, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I, _P]),
     "paged_attn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "pkv_strerror": (ctypes.c_char_p, [_I]),
     "pkv_validate_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
@@ -42,6 +44,8 @@ _SIGNATURES = {
     "pkv_validate_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64,
                                  _F, _I, _I, _P, _P, _P, _I]),
     "pkv_validate_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I]),
+    "pkv_validate_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                               _I64, _F, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I]),
 }
 
 
@@ -233,3 +237,60 @@ def decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale, *, k_
                       k_scale=k_scale, v_scale=v_scale, partition_size=partition_size,
                       part_out=po, part_max=pm, part_sum=ps, stream=stream)
     paged_attn_reduce(out, po, pm, ps, context_lens, partition_size, stream=stream)
+
+
+def alloc_step_workspace(B, Hq, Hkv, D, max_partitions, device="cuda"):
+    """(part_out, part_max, part_sum, counters) for paged_decode_step; the
+    counters start at zero and every call leaves them at zero."""
+    po, pm, ps = alloc_partials(B, Hq, D, max_partitions, device)
+    counters = torch.zeros((B, Hkv), dtype=torch.int32, device=device)
+    return po, pm, ps, counters
+
+
+def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale, *, k_new=None,
+                      v_new=None, k_scale=None, v_scale=None, partition_size=0, gamma_q=None,
+                      gamma_k=None, eps=1e-6, rope_theta=1e6, workspace=None, stream=None):
+    """Append (optional, + Qwen3 QK-norm/RoPE) + decode + combine in one launch.
+    ``workspace`` is alloc_step_workspace(...)'s tuple (needed when
+    partition_size > 0)."""
+    _check(out, "out", torch.float16, 3)
+    _check(q, "q", torch.float16, 3)
+    kv = _kv_dtype(k_pool)
+    _check(k_pool, "k_pool", k_pool.dtype, 4)
+    _check(v_pool, "v_pool", k_pool.dtype, 4)
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(context_lens, "context_lens", torch.int32, 1)
+    B, Hq, D = q.shape
+    NB, Hkv, BS, d2 = k_pool.shape
+    if d2 != D or v_pool.shape != k_pool.shape or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("q / out / pool shapes disagree")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens must have B rows")
+    if kv == PKV_KV_E4M3:
+        _check(k_scale, "k_scale", torch.float32, 2)
+        _check(v_scale, "v_scale", torch.float32, 2)
+    if k_new is not None:
+        _check(k_new, "k_new", torch.float16, 3)
+        _check(v_new, "v_new", torch.float16, 3)
+        if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+            raise ValueError("k_new / v_new must be [B, Hkv, D]")
+    if gamma_k is not None:
+        _check(gamma_q, "gamma_q", torch.float32, 1)
+        _check(gamma_k, "gamma_k", torch.float32, 1)
+    po = pm = ps = ctr = None
+    P = 1
+    if partition_size:
+        if workspace is None:
+            raise ValueError("partition_size > 0 needs a workspace (alloc_step_workspace)")
+        po, pm, ps, ctr = workspace
+        _check(ctr, "counters", torch.int32, 2)
+        P = po.shape[2]
+        if tuple(po.shape) != (B, Hq, P, D) or tuple(ctr.shape) != (B, Hkv):
+            raise ValueError("workspace shapes disagree")
+    st = lib().paged_decode_step(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                 _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                 _ptr(context_lens), B, Hq, Hkv, D, BS, block_tables.shape[1], NB,
+                                 float(scale), kv, int(partition_size), _ptr(gamma_q),
+                                 _ptr(gamma_k), float(eps), float(rope_theta), _ptr(po), _ptr(pm),
+                                 _ptr(ps), _ptr(ctr), P, _stream(stream))
+    _raise("paged_decode_step", st)

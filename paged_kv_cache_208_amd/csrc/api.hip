@@ -85,3 +85,50 @@ extern "C" int paged_attn_reduce(void* out, const float* part_out, const float* 
                     Hq, D, partition_size, max_partitions};
   return launch_status(pkv::launch_reduce(a, B, static_cast<hipStream_t>(stream)));
 }
+
+extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const void* v_new,
+                                 void* k_pool, void* v_pool, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_tables,
+                                 const int32_t* context_lens, int B, int Hq, int Hkv, int D,
+                                 int BS, int MBS, int64_t NB, float scale, int kv_dtype,
+                                 int partition_size, const float* gamma_q, const float* gamma_k,
+                                 float eps, float rope_theta, float* part_out, float* part_max,
+                                 float* part_sum, uint32_t* counters, int max_partitions,
+                                 void* stream) {
+  const int st = pkv_validate_step(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
+                                   block_tables, context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale,
+                                   kv_dtype, partition_size, gamma_q, gamma_k, eps, rope_theta,
+                                   part_out, part_max, part_sum, counters, max_partitions);
+  if (st != PKV_OK || B == 0) return st;
+  const bool fp8 = kv_dtype == PKV_KV_E4M3;
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.k_scale = fp8 ? k_scale : nullptr;
+  a.v_scale = fp8 ? v_scale : nullptr;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.part_out = part_out;
+  a.part_max = part_max;
+  a.part_sum = part_sum;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.MBS = MBS;
+  a.partition_size = partition_size;
+  a.max_partitions = partition_size ? max_partitions : 1;
+  a.scale_log2 = scale * pkv::kLog2e;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.gamma_q = gamma_q;
+  a.gamma_k = gamma_k;
+  a.eps = eps;
+  a.theta = rope_theta;
+  a.counters = counters;
+  int mode = pkv::kModeCombine;
+  if (k_new) mode |= pkv::kModeAppend;
+  if (gamma_k) mode |= pkv::kModeQkNorm;
+  return launch_status(pkv::launch_decode_step(a, B, D, Hq / Hkv, fp8, mode,
+                                               static_cast<hipStream_t>(stream)));
+}

@@ -28,8 +28,11 @@
 //  * VALU: 16-byte K/V slices per lane, v_dot2 partial logits completed by
 //    DPP row reductions, fp32 FMAs for P.V.  About 430 VALU instructions
 //    per fp16 tile.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
+#include "shape_limits.h"
 
 // Tuning knobs (compile-time): waves per workgroup, the occupancy the
 // register allocator is asked to reach (waves per SIMD), and the order in
@@ -63,6 +66,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Unit {
   int b, kvh, p;
+  int L;               // context length of the sequence
   int tok_lo, tok_hi;  // token range of the unit
   int n_lo, n_hi;      // logical block range
   bool empty;          // partitioned and past the context: nothing to write
@@ -84,6 +88,7 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a) {
   u.kvh = x % a.Hkv;
   u.b = x / a.Hkv;
   const int L = a.context_lens[u.b];
+  u.L = L;
   u.tok_lo = 0;
   u.tok_hi = L;
   u.empty = false;
@@ -143,12 +148,29 @@ __device__ __forceinline__ int tile_base(const DecodeArgs& a, const TileWalk<NW>
 // so its wait for that tile's data) above the next tile's loads.
 __device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Combine the NW waves' (m, l, acc) held in LDS and write the result.
+// Partition statistics handed from one workgroup to another inside a launch
+// are written and read with device-scope (agent) relaxed atomics, which the
+// hardware keeps coherent across the XCDs' separate L2 caches without
+// writing back or invalidating whole caches.  Ordinary accesses are used
+// when the handoff happens across launches.
+template <bool COHERENT>
+__device__ __forceinline__ void store_f32(float* p, float v) {
+  if constexpr (COHERENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
+__device__ __forceinline__ float load_f32_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Combine the NW waves' (m, l, acc) held in LDS and write the result: the
+// fp16 output when `direct` (single pass, or a context that fits one
+// partition in the step kernel), else the unit's partition statistics.
 // m is in log2 units of the scaled logit; acc is unnormalised.
-template <int D, int G, int NW>
+template <int D, int G, int NW, bool COHERENT = false>
 __device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const Unit& u,
                                                   float (*s_acc)[G][D], float (*s_m)[G],
-                                                  float (*s_l)[G]) {
+                                                  float (*s_l)[G], bool direct) {
   const int h0 = u.kvh * G;
   for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
     const int j = idx / D;
@@ -164,18 +186,86 @@ __device__ __forceinline__ void combine_and_store(const DecodeArgs& a, const Uni
       num = fmaf(s_acc[w][j][d], f, num);
     }
     const size_t row = size_t(u.b) * a.Hq + h0 + j;
-    if (a.partition_size == 0) {
+    if (direct) {
       // an empty context is a zero row; anything else divides, so a NaN that
       // reached the sums stays visible
       static_cast<_Float16*>(a.out)[row * D + d] = (_Float16)(u.tok_hi > 0 ? num / den : 0.0f);
     } else {
       const size_t pr = row * a.max_partitions + u.p;
-      a.part_out[pr * D + d] = num / den;
+      store_f32<COHERENT>(a.part_out + pr * D + d, num / den);
       if (d == 0) {
-        a.part_max[pr] = M * kLn2;
-        a.part_sum[pr] = den;
+        store_f32<COHERENT>(a.part_max + pr, M * kLn2);
+        store_f32<COHERENT>(a.part_sum + pr, den);
       }
     }
+  }
+}
+
+// Log-sum-exp combine of the P partitions of the unit's G heads, written as
+// the fp16 output (the same arithmetic as paged_attn_reduce, partitions in
+// ascending order).  The (m, l) pairs are fetched in parallel into LDS, then
+// each output element's P partial values are loaded eight at a time so their
+// latencies overlap.
+template <int D, int G, int NW>
+__device__ __forceinline__ void combine_partitions(const DecodeArgs& a, const Unit& u, int P) {
+  __shared__ float s_pm[G][kMaxStepPartitions];  // the host check bounds P by this
+  __shared__ float s_pw[G][kMaxStepPartitions];
+  const size_t row0 = size_t(u.b) * a.Hq + u.kvh * G;
+  for (int t = threadIdx.x; t < G * P; t += NW * kWave) {
+    const int j = t / P, p = t % P;
+    const size_t pr = (row0 + j) * a.max_partitions + p;
+    s_pm[j][p] = load_f32_coherent(a.part_max + pr);
+    s_pw[j][p] = load_f32_coherent(a.part_sum + pr);
+  }
+  __syncthreads();
+  // weights w_p = l_p exp(m_p - M) per head, in place
+  for (int j = threadIdx.x; j < G; j += NW * kWave) {
+    float M = -FLT_MAX;
+    for (int p = 0; p < P; ++p) M = fmaxf(M, s_pm[j][p]);
+    float den = 0.0f;
+    for (int p = 0; p < P; ++p) {
+      const float wgt = s_pw[j][p] * fast_exp2((s_pm[j][p] - M) * kLog2e);
+      den += wgt;
+      s_pw[j][p] = wgt;
+    }
+    s_pm[j][0] = den;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave) {
+    const int j = idx / D;
+    const int d = idx % D;
+    const float* po = a.part_out + (row0 + j) * a.max_partitions * D + d;
+    float num = 0.0f;
+    for (int p0 = 0; p0 < P; p0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = p0 + k < P ? load_f32_coherent(po + size_t(p0 + k) * D) : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (p0 + k < P) num = fmaf(s_pw[j][p0 + k], v[k], num);
+    }
+    static_cast<_Float16*>(a.out)[(row0 + j) * D + d] = (_Float16)(num / s_pm[j][0]);
+  }
+}
+
+// Zero output rows of the unit's G heads (empty context).
+template <int D, int G, int NW>
+__device__ __forceinline__ void store_zero_rows(const DecodeArgs& a, const Unit& u) {
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * kWave)
+    static_cast<_Float16*>(a.out)[(size_t(u.b) * a.Hq + u.kvh * G) * D + idx] = (_Float16)0.0f;
+}
+
+// cos / sin of the split-half RoPE angles pos * theta^(-2i/D), i < D/2,
+// evaluated in fp64 once per workgroup ("Roadmap: vLLM-style serving features
+// for TornadoVM batched decode", Core batched decode: Qwen3 split-half RoPE).
+template <int D, int NW>
+__device__ __forceinline__ void rope_table(float* s_cos, float* s_sin, int pos, float theta) {
+  for (int i = threadIdx.x; i < D / 2; i += NW * kWave) {
+    const double ang = double(pos) * pow(double(theta), -2.0 * double(i) / double(D));
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    s_cos[i] = float(cs);
+    s_sin[i] = float(sn);
   }
 }
 
@@ -363,17 +453,73 @@ __device__ __forceinline__ void mfma_tile(MState<D, FP8>& st, const MTile<D, FP8
     st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v_operand<D, FP8>(t, i), pv, st.acc[i], 0, 0, 0);
 }
 
-template <int D, int G, bool FP8, int NW>
+// RMSNorm over the head (its four lane groups) and split-half RoPE of the
+// head held in the lane's QK chunks: chunk c of lane group g covers dims
+// 32c + 8g + 0..7, so chunk c + D/64 holds the rotation partners (dims
+// + D/2) of chunk c in the same lane.  fp32 arithmetic, angles from the
+// fp64 table, one rounding to fp16.
+template <int D>
+__device__ __forceinline__ void norm_rope_chunks(half8_t* x, const float* gamma, float eps,
+                                                 const float* s_cos, const float* s_sin, int g) {
+  constexpr int NC = D / 32, HALF = NC / 2;
+  float v[NC][8];
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[c][e] = float(x[c][e]);
+      ss = fmaf(v[c][e], v[c][e], ss);
+    }
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  const float inv = 1.0f / sqrtf(ss / float(D) + eps);
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[c][e] = v[c][e] * inv * gamma[qk_dim0<false>(c, g) + e];
+#pragma unroll
+  for (int c = 0; c < HALF; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = qk_dim0<false>(c, g) + e;
+      const float cs = s_cos[i], sn = s_sin[i];
+      const float lo = v[c][e], hi = v[c + HALF][e];
+      x[c][e] = (_Float16)fmaf(lo, cs, -hi * sn);
+      x[c + HALF][e] = (_Float16)fmaf(hi, cs, lo * sn);
+    }
+}
+
+template <int D, int G, bool FP8, int NW, int MODE>
 __global__ PKV_DECODE_BOUNDS(NW) void decode_mfma_kernel(DecodeArgs a) {
   using Geo = MfmaGeo<D, FP8>;
+  constexpr bool APPEND = (MODE & kModeAppend) != 0;
+  constexpr bool QKNORM = (MODE & kModeQkNorm) != 0;
+  constexpr bool COMBINE = (MODE & kModeCombine) != 0;
   static_assert(G <= 16, "head slots of one 16-wide product");
+  static_assert(!(APPEND && FP8), "the step kernel appends fp16 rows only");
+  static_assert(!QKNORM || APPEND, "QK-norm comes with the append of the new row");
   const Unit u = decode_unit(a);
-  if (u.empty) return;  // whole workgroup
+  if (u.empty) {  // whole workgroup: a partition past the context
+    if constexpr (COMBINE)
+      if (u.p == 0) store_zero_rows<D, G, NW>(a, u);  // empty context: zero row
+    return;
+  }
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane / 16;
   const int n16 = lane % 16;
+  const int32_t* trow = a.block_tables + size_t(u.b) * a.MBS;
+  const int k_off = n16 * Geo::kRow + g * 16;
+  const int v_off = (4 * g) * Geo::kRow + n16 * Geo::kVBytes;
+
+  __shared__ float s_cos[QKNORM ? D / 2 : 1];
+  __shared__ float s_sin[QKNORM ? D / 2 : 1];
+  if constexpr (QKNORM) {
+    rope_table<D, NW>(s_cos, s_sin, u.L - 1, a.theta);
+    __syncthreads();
+  }
 
   // B operand of the QK products: q of head slot n16 (zero past the group)
   half8_t qop[Geo::kQK];
@@ -381,9 +527,45 @@ __global__ PKV_DECODE_BOUNDS(NW) void decode_mfma_kernel(DecodeArgs a) {
     const _Float16* qh =
         static_cast<const _Float16*>(a.q) + (size_t(u.b) * a.Hq + u.kvh * G + min(n16, G - 1)) * D;
 #pragma unroll
-    for (int c = 0; c < Geo::kQK; ++c) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(qh + qk_dim0<FP8>(c, g));
-      qop[c] = n16 < G ? __builtin_bit_cast(half8_t, x) : half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int c = 0; c < Geo::kQK; ++c)
+      qop[c] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(qh + qk_dim0<FP8>(c, g)));
+    if constexpr (QKNORM) norm_rope_chunks<D>(qop, a.gamma_q, a.eps, s_cos, s_sin, g);
+    if (n16 >= G)
+#pragma unroll
+      for (int c = 0; c < Geo::kQK; ++c) qop[c] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  // The step's new row (token L-1) lives in the last tile of the unit that
+  // ends the context.  The wave that will read that tile writes it first,
+  // each lane storing exactly the 16-byte pieces it later loads, so the
+  // loads observe the stores (same lane, same address, program order).
+  if constexpr (APPEND) {
+    if (u.tok_hi == u.L) {
+      const int t = u.L - 1;
+      const int n_last = t / 16, r_new = t % 16;
+      if (w == (n_last - u.n_lo) % NW) {
+        const int id = __builtin_amdgcn_readfirstlane(trow[n_last]);
+        const size_t base = (size_t(id) * a.Hkv + u.kvh) * Geo::kTile;
+        const size_t row = size_t(u.b) * a.Hkv + u.kvh;
+        const _Float16* kn = static_cast<const _Float16*>(a.k_new) + row * D;
+        const _Float16* vn = static_cast<const _Float16*>(a.v_new) + row * D;
+        half8_t kc[Geo::kKLoads];
+#pragma unroll
+        for (int i = 0; i < Geo::kKLoads; ++i)
+          kc[i] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(kn + (4 * i + g) * 8));
+        if constexpr (QKNORM) norm_rope_chunks<D>(kc, a.gamma_k, a.eps, s_cos, s_sin, g);
+        uint8_t* kt = const_cast<uint8_t*>(a.k_pool) + base;
+        uint8_t* vt = const_cast<uint8_t*>(a.v_pool) + base;
+        if (n16 == r_new)
+#pragma unroll
+          for (int i = 0; i < Geo::kKLoads; ++i)
+            *reinterpret_cast<u32x4*>(kt + k_off + i * 64) = __builtin_bit_cast(u32x4, kc[i]);
+        if (g == r_new / 4) {
+          using VW = typename Words<Geo::kVWords>::T;
+          *reinterpret_cast<VW*>(vt + v_off + (r_new % 4) * Geo::kRow) =
+              *reinterpret_cast<const VW*>(vn + n16 * (D / 16));
+        }
+      }
     }
   }
 
@@ -394,10 +576,7 @@ __global__ PKV_DECODE_BOUNDS(NW) void decode_mfma_kernel(DecodeArgs a) {
   for (int i = 0; i < Geo::kPV; ++i) st.acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   TileWalk<NW> walk;
-  walk.init(a.block_tables + size_t(u.b) * a.MBS, u, w);
-  const int k_off = n16 * Geo::kRow + g * 16;
-  const int v_off = (4 * g) * Geo::kRow + n16 * Geo::kVBytes;
-
+  walk.init(trow, u, w);
   MTile<D, FP8> ta, tb;
   for (int c0 = 0; c0 < walk.count; c0 += kWave) {
     walk.fill(c0);
@@ -432,7 +611,42 @@ __global__ PKV_DECODE_BOUNDS(NW) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  combine_and_store<D, G, NW>(a, u, s_acc, s_m, s_l);
+
+  // number of partitions of this sequence (1 for a single pass)
+  const int P = a.partition_size ? (u.L + a.partition_size - 1) / a.partition_size : 1;
+  const bool direct = a.partition_size == 0 || (COMBINE && P == 1);
+  combine_and_store<D, G, NW, COMBINE>(a, u, s_acc, s_m, s_l, direct);
+
+  bool finisher = direct;  // writes q' back: the last workgroup of the (b, kv head)
+  if constexpr (COMBINE) {
+    if (!direct) {
+      // Publish this partition and count arrivals; the last one combines.
+      // The barrier waits for every thread's (coherent) partial stores to
+      // complete before thread 0 increments the counter, and the last
+      // workgroup reads the partials only after its increment returned.
+      __shared__ int s_last;
+      __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+      __syncthreads();
+      uint32_t* ctr = a.counters + size_t(u.b) * a.Hkv + u.kvh;
+      if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 uint32_t(P - 1);
+      __syncthreads();
+      if (!s_last) return;  // whole workgroup
+      combine_partitions<D, G, NW>(a, u, P);
+      if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      finisher = true;
+    }
+  }
+  if constexpr (QKNORM) {
+    if (finisher && w == 0 && n16 < G) {
+      _Float16* qh = const_cast<_Float16*>(static_cast<const _Float16*>(a.q)) +
+                     (size_t(u.b) * a.Hq + u.kvh * G + n16) * D;
+#pragma unroll
+      for (int c = 0; c < Geo::kQK; ++c)
+        *reinterpret_cast<u32x4*>(qh + qk_dim0<false>(c, g)) = __builtin_bit_cast(u32x4, qop[c]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -670,7 +884,7 @@ __global__ PKV_DECODE_VALU_BOUNDS(NW) void decode_valu_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  combine_and_store<D, G, NW>(a, u, s_acc, s_m, s_l);
+  combine_and_store<D, G, NW>(a, u, s_acc, s_m, s_l, a.partition_size == 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -678,28 +892,66 @@ __global__ PKV_DECODE_VALU_BOUNDS(NW) void decode_valu_kernel(DecodeArgs a) {
 
 constexpr int kWavesPerGroup = PKV_DECODE_WAVES;
 
+template <int D, int G, bool FP8, int MODE>
+hipError_t launch_mfma(const DecodeArgs& a, int B, hipStream_t stream) {
+  const unsigned units = unsigned(int64_t(B) * a.Hkv * a.max_partitions);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G, FP8, kWavesPerGroup, MODE>), dim3(units),
+                     dim3(kWavesPerGroup * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, int G, bool FP8>
 hipError_t launch_typed(const DecodeArgs& a, int B, DecodeEngine engine, hipStream_t stream) {
-  const unsigned units = unsigned(int64_t(B) * a.Hkv * a.max_partitions);
-  if (engine == DecodeEngine::kValu)
+  if (engine == DecodeEngine::kValu) {
+    const unsigned units = unsigned(int64_t(B) * a.Hkv * a.max_partitions);
     hipLaunchKernelGGL((decode_valu_kernel<D, G, FP8, kWavesPerGroup>), dim3(units),
                        dim3(kWavesPerGroup * kWave), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G, FP8, kWavesPerGroup>), dim3(units),
-                       dim3(kWavesPerGroup * kWave), 0, stream, a);
-  return hipGetLastError();
+    return hipGetLastError();
+  }
+  return launch_mfma<D, G, FP8, kModeAttend>(a, B, stream);
+}
+
+template <int D, int G, bool FP8>
+hipError_t launch_step_typed(const DecodeArgs& a, int B, int mode, hipStream_t stream) {
+  if constexpr (FP8) {
+    if (mode == kModeCombine) return launch_mfma<D, G, true, kModeCombine>(a, B, stream);
+    return hipErrorInvalidValue;
+  } else {
+    switch (mode) {
+      case kModeCombine: return launch_mfma<D, G, false, kModeCombine>(a, B, stream);
+      case kModeAppend | kModeCombine:
+        return launch_mfma<D, G, false, kModeAppend | kModeCombine>(a, B, stream);
+      case kModeAppend | kModeQkNorm | kModeCombine:
+        return launch_mfma<D, G, false, kModeAppend | kModeQkNorm | kModeCombine>(a, B, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
+template <int D, bool FP8, typename F>
+hipError_t by_group(int group, F&& f) {
+  switch (group) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int D, bool FP8>
 hipError_t launch_group(const DecodeArgs& a, int B, int group, DecodeEngine engine,
                         hipStream_t stream) {
-  switch (group) {
-    case 1: return launch_typed<D, 1, FP8>(a, B, engine, stream);
-    case 2: return launch_typed<D, 2, FP8>(a, B, engine, stream);
-    case 4: return launch_typed<D, 4, FP8>(a, B, engine, stream);
-    case 8: return launch_typed<D, 8, FP8>(a, B, engine, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return by_group<D, FP8>(group, [&](auto gc) {
+    return launch_typed<D, decltype(gc)::value, FP8>(a, B, engine, stream);
+  });
+}
+
+template <int D, bool FP8>
+hipError_t launch_step_group(const DecodeArgs& a, int B, int group, int mode, hipStream_t stream) {
+  return by_group<D, FP8>(group, [&](auto gc) {
+    return launch_step_typed<D, decltype(gc)::value, FP8>(a, B, mode, stream);
+  });
 }
 
 }  // namespace
@@ -710,6 +962,15 @@ hipError_t launch_decode(const DecodeArgs& a, int B, int D, int group, bool fp8,
                            : launch_group<128, false>(a, B, group, engine, stream);
   if (D == 64) return fp8 ? launch_group<64, true>(a, B, group, engine, stream)
                           : launch_group<64, false>(a, B, group, engine, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_step(const DecodeArgs& a, int B, int D, int group, bool fp8, int mode,
+                              hipStream_t stream) {
+  if (D == 128) return fp8 ? launch_step_group<128, true>(a, B, group, mode, stream)
+                           : launch_step_group<128, false>(a, B, group, mode, stream);
+  if (D == 64) return fp8 ? launch_step_group<64, true>(a, B, group, mode, stream)
+                          : launch_step_group<64, false>(a, B, group, mode, stream);
   return hipErrorInvalidValue;
 }
 

@@ -7,9 +7,9 @@
 namespace pkv {
 
 struct DecodeArgs {
-  void* out;                  // [B][Hq][D] fp16, single pass only
-  const void* q;              // [B][Hq][D] fp16
-  const uint8_t* k_pool;      // [NB][Hkv][16][D] fp16 or E4M3
+  void* out;                  // [B][Hq][D] fp16: single pass, or combined in the step kernel
+  const void* q;              // [B][Hq][D] fp16 (step kernel with QK-norm: rewritten in place)
+  const uint8_t* k_pool;      // [NB][Hkv][16][D] fp16 or E4M3 (step kernel: the new row is written)
   const uint8_t* v_pool;
   const float* k_scale;       // [NB][Hkv], E4M3 only
   const float* v_scale;
@@ -22,6 +22,21 @@ struct DecodeArgs {
   int partition_size;         // 0 = single pass
   int max_partitions;         // P (partitioned) or 1
   float scale_log2;           // softmax scale * log2(e)
+  // decode step only
+  const void* k_new;          // [B][Hkv][D] fp16: row of token L_b - 1
+  const void* v_new;
+  const float* gamma_q;       // [D] (QK-norm)
+  const float* gamma_k;
+  float eps, theta;
+  uint32_t* counters;         // [B][Hkv] arrivals per (sequence, kv head); zero between launches
+};
+
+// What a decode launch does besides attending (bit flags).
+enum DecodeMode : int {
+  kModeAttend = 0,
+  kModeAppend = 1,    // write each sequence's new K/V row before reading it
+  kModeQkNorm = 2,    // Qwen3 QK-RMSNorm + split-half RoPE of q and the new k
+  kModeCombine = 4,   // the last workgroup of each (sequence, kv head) combines partitions
 };
 
 struct ReduceArgs {
@@ -53,6 +68,8 @@ enum class DecodeEngine { kMfma, kValu };
 // Launchers return the hipError_t of the launch.
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, int group, bool fp8,
                          DecodeEngine engine, hipStream_t stream);
+hipError_t launch_decode_step(const DecodeArgs& a, int B, int D, int group, bool fp8, int mode,
+                              hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int B, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int T, int D, bool fused, hipStream_t stream);
 

@@ -9,4 +9,5 @@ constexpr int kMaxPartition = 16384;      // tokens per split-context partition
 constexpr int64_t kMaxContext = int64_t(1) << 24;   // MBS * BS
 constexpr int64_t kMaxGrid = (int64_t(1) << 24) - 1;  // workgroups per launch (x <= 2^32 / 256)
 constexpr int64_t kMaxAppendRows = int64_t(1) << 24;
+constexpr int kMaxStepPartitions = 64;     // partitions one step combines in-kernel
 }  // namespace pkv

@@ -124,3 +124,41 @@ extern "C" int pkv_validate_reduce(const void* out, const float* part_out,
     return PKV_EINVAL;
   return PKV_OK;
 }
+
+extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_new,
+                                 const void* v_new, const void* k_pool, const void* v_pool,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, const int32_t* context_lens, int B,
+                                 int Hq, int Hkv, int D, int BS, int MBS, int64_t NB, float scale,
+                                 int kv_dtype, int partition_size, const float* gamma_q,
+                                 const float* gamma_k, float eps, float rope_theta,
+                                 const float* part_out, const float* part_max,
+                                 const float* part_sum, const uint32_t* counters,
+                                 int max_partitions) {
+  // the attention part is checked exactly as paged_attn_decode checks it
+  int st = pkv_validate_decode(out, q, k_pool, v_pool, k_scale, v_scale, block_tables,
+                               context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale, kv_dtype,
+                               partition_size, part_out, part_max, part_sum, max_partitions);
+  if (st != PKV_OK || B == 0) return st;
+  if (!out || !aligned(out, 16)) return PKV_EINVAL;
+  if (partition_size != 0) {
+    if (!counters || !aligned(counters, 4)) return PKV_EINVAL;
+    // the in-kernel combine holds at most 64 partitions per sequence
+    if ((int64_t(MBS) * BS + partition_size - 1) / partition_size > pkv::kMaxStepPartitions)
+      return PKV_EUNSUPPORTED;
+  }
+  if (k_new != nullptr) {
+    if (kv_dtype != PKV_KV_F16) return PKV_EUNSUPPORTED;
+    if (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return PKV_EINVAL;
+  } else if (v_new != nullptr) {
+    return PKV_EINVAL;
+  }
+  if (gamma_k != nullptr) {
+    if (!k_new || !gamma_q || !aligned(gamma_q, 4) || !aligned(gamma_k, 4)) return PKV_EINVAL;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return PKV_EINVAL;
+    if (!(rope_theta > 0.0f) || !std::isfinite(rope_theta)) return PKV_EINVAL;
+  } else if (gamma_q != nullptr) {
+    return PKV_EINVAL;
+  }
+  return PKV_OK;
+}

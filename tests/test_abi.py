@@ -166,3 +166,41 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def _step_args(**kw):
+    a = dict(out=A, q=A, k_new=A, v_new=A, k_pool=A, v_pool=A, k_scale=None, v_scale=None,
+             block_tables=A, context_lens=A, B=2, Hq=8, Hkv=2, D=128, BS=16, MBS=8, NB=100,
+             scale=0.1, kv_dtype=0, partition_size=64, gamma_q=None, gamma_k=None, eps=1e-6,
+             theta=1e6, part_out=A, part_max=A, part_sum=A, counters=A, max_partitions=2)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    (dict(partition_size=0, counters=None, part_out=None, part_max=None, part_sum=None), 0),
+    (dict(B=0, out=None), 0),
+    (dict(out=None), -1),
+    (dict(counters=None), -1),
+    (dict(counters=A + 2), -1),
+    (dict(v_new=None), -1),
+    (dict(k_new=None), -1),
+    (dict(k_new=None, v_new=None), 0),
+    (dict(k_new=A + 8), -1),
+    (dict(gamma_k=A), -1),
+    (dict(gamma_k=A, gamma_q=A), 0),
+    (dict(gamma_q=A), -1),
+    (dict(gamma_k=A, gamma_q=A, k_new=None, v_new=None), -1),
+    (dict(gamma_k=A, gamma_q=A, theta=-1.0), -1),
+    (dict(kv_dtype=1, k_scale=A, v_scale=A), -2),
+    (dict(kv_dtype=1, k_scale=A, v_scale=A, k_new=None, v_new=None), 0),
+    (dict(D=96), -2),
+    (dict(max_partitions=1), -1),
+    (dict(partition_size=16, MBS=65, max_partitions=65), -2),
+    (dict(partition_size=16, MBS=64, max_partitions=64), 0),
+])
+def test_step_validation_codes(lib, kw, code):
+    assert lib.pkv_validate_step(*_step_args(**kw).values()) == code
+    if code != 0:
+        assert lib.paged_decode_step(*_step_args(**kw).values(), None) == code
