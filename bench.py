@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--partition-size", type=int, default=None)
     p.add_argument("--rotate", type=int, default=None, help="copies of the inputs (default: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--splits", type=int, default=16,
+                   help="most pieces one sequence is cut into by the balanced split")
     p.add_argument("--unfused", action="store_true",
                    help="time append, decode and reduce as three launches")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -162,7 +164,10 @@ def main():
     PS = cfg.partition_size
     P = _lib.max_partitions_for(cfg.mbs, PS)
     ws = _lib.alloc_partials(B, Hq, D, P, dev) if PS else None
-    step_ws = _lib.alloc_step_workspace(B, Hq, cfg.Hkv, D, P, dev) if PS else None
+    # the one-launch step splits contexts evenly over all waves (partition_size 0)
+    # unless --partition-size asks for fixed partitions
+    step_ps = PS if args.partition_size is not None else 0
+    step_ws = _lib.alloc_step_workspace(B, Hq, cfg.Hkv, D, P if step_ps else args.splits, dev)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     fp8 = cfg.kv_dtype == "e4m3"
     torch.cuda.synchronize()
@@ -201,8 +206,8 @@ def main():
             ev["d0"][i].record(stream)
         _lib.paged_decode_step(out, g["q"], g["k_pool"], g["v_pool"], g["block_tables"],
                                g["context_lens"], cfg.scale, k_scale=g.get("k_scale"),
-                               v_scale=g.get("v_scale"), partition_size=PS, workspace=step_ws,
-                               stream=stream, **kw)
+                               v_scale=g.get("v_scale"), partition_size=step_ps,
+                               workspace=step_ws, stream=stream, **kw)
         if timed:
             ev["d1"][i].record(stream)
 
@@ -258,7 +263,9 @@ def main():
             "workload": cfg.description,
             "name": cfg.name,
             "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "head_dim": cfg.D, "block_size": 16,
-            "kv_dtype": cfg.kv_dtype, "partition_size": PS,
+            "kv_dtype": cfg.kv_dtype,
+            "split": (f"fixed {PS}-token partitions" if args.unfused or step_ps
+                      else f"balanced over all waves, <= {args.splits} pieces per sequence"),
             "context_tokens": tokens, "mean_context": round(tokens / cfg.B, 1),
             "step": ("attend+combine" if fp8 else
                      ("qknorm_rope+append+attend+combine" if cfg.fused_append

@@ -150,16 +150,22 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
  *     pos = L_b - 1 is first applied to the new k and to q, which is
  *     rewritten in place, exactly as paged_kv_append does;
  *  2. q attends over the sequence's paged KV as in paged_attn_decode;
- *  3. with partition_size > 0, the last workgroup to finish for each
- *     (sequence, kv head) combines its partitions as paged_attn_reduce does,
- *     so out [B][Hq][D] fp16 is complete when the launch is.
- * counters: [B][Hkv] uint32 device memory, all zero before the first call;
- *   each call leaves them zero again.  Calls sharing counters, partials or
- *   pools must not run concurrently.  part_* are scratch as for
- *   paged_attn_decode (contents undefined afterwards).
- * partition_size 0: single pass; counters and part_* are not used.
- * partition_size > 0: at most 64 partitions per sequence
+ *  3. each sequence's context is split into pieces that different
+ *     workgroups read in parallel, and the last piece to finish for each
+ *     (sequence, kv head) combines them as paged_attn_reduce does, so out
+ *     [B][Hq][D] fp16 is complete when the launch is.
+ * partition_size == 0: balanced split.  The library gives every wave the
+ *   same number of 16-token tiles of the whole batch (whatever the mix of
+ *   context lengths); a sequence is cut into at most max_partitions pieces
+ *   (3 <= max_partitions <= 64).
+ * partition_size > 0: fixed partitions of that many tokens as in
+ *   paged_attn_decode, at most 64 per sequence
  *   (ceil(MBS * BS / partition_size) <= 64), else PKV_EUNSUPPORTED.
+ * part_out / part_max / part_sum: [B][Hq][max_partitions]([D]) fp32 scratch
+ *   (contents undefined afterwards).  counters: [B][Hkv] uint32 device
+ *   memory, all zero before the first call; each call leaves them zero
+ *   again.  Calls sharing counters, scratch or pools must not run
+ *   concurrently.
  * kv_dtype PKV_KV_E4M3: attend + combine only (k_new must be NULL).
  * L_b == 0: zero output row, nothing written to the pools, q untouched.
  * Errors and shape limits as for paged_attn_decode and paged_kv_append.

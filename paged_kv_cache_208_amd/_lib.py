@@ -251,8 +251,9 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                       v_new=None, k_scale=None, v_scale=None, partition_size=0, gamma_q=None,
                       gamma_k=None, eps=1e-6, rope_theta=1e6, workspace=None, stream=None):
     """Append (optional, + Qwen3 QK-norm/RoPE) + decode + combine in one launch.
-    ``workspace`` is alloc_step_workspace(...)'s tuple (needed when
-    partition_size > 0)."""
+    ``workspace`` is alloc_step_workspace(...)'s tuple.  partition_size 0
+    splits contexts evenly over all waves into at most workspace-depth
+    pieces; > 0 uses fixed partitions."""
     _check(out, "out", torch.float16, 3)
     _check(q, "q", torch.float16, 3)
     kv = _kv_dtype(k_pool)
@@ -277,16 +278,15 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
     if gamma_k is not None:
         _check(gamma_q, "gamma_q", torch.float32, 1)
         _check(gamma_k, "gamma_k", torch.float32, 1)
-    po = pm = ps = ctr = None
-    P = 1
-    if partition_size:
-        if workspace is None:
-            raise ValueError("partition_size > 0 needs a workspace (alloc_step_workspace)")
-        po, pm, ps, ctr = workspace
-        _check(ctr, "counters", torch.int32, 2)
-        P = po.shape[2]
-        if tuple(po.shape) != (B, Hq, P, D) or tuple(ctr.shape) != (B, Hkv):
-            raise ValueError("workspace shapes disagree")
+    if workspace is None:
+        raise ValueError("paged_decode_step needs a workspace (alloc_step_workspace)")
+    po, pm, ps, ctr = workspace
+    _check(po, "part_out", torch.float32, 4)
+    _check(ctr, "counters", torch.int32, 2)
+    P = po.shape[2]
+    if (tuple(po.shape) != (B, Hq, P, D) or tuple(pm.shape) != (B, Hq, P)
+            or tuple(ps.shape) != (B, Hq, P) or tuple(ctr.shape) != (B, Hkv)):
+        raise ValueError("workspace shapes disagree")
     st = lib().paged_decode_step(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
                                  _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                                  _ptr(context_lens), B, Hq, Hkv, D, BS, block_tables.shape[1], NB,

@@ -117,7 +117,7 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
   a.Hkv = Hkv;
   a.MBS = MBS;
   a.partition_size = partition_size;
-  a.max_partitions = partition_size ? max_partitions : 1;
+  a.max_partitions = max_partitions;
   a.scale_log2 = scale * pkv::kLog2e;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -129,6 +129,9 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
   int mode = pkv::kModeCombine;
   if (k_new) mode |= pkv::kModeAppend;
   if (gamma_k) mode |= pkv::kModeQkNorm;
+  if (partition_size == 0)  // balanced split across a fixed number of waves
+    return launch_status(pkv::launch_decode_stream(a, B, D, Hq / Hkv, fp8, mode,
+                                                   static_cast<hipStream_t>(stream)));
   return launch_status(pkv::launch_decode_step(a, B, D, Hq / Hkv, fp8, mode,
                                                static_cast<hipStream_t>(stream)));
 }

@@ -70,6 +70,8 @@ hipError_t launch_decode(const DecodeArgs& a, int B, int D, int group, bool fp8,
                          DecodeEngine engine, hipStream_t stream);
 hipError_t launch_decode_step(const DecodeArgs& a, int B, int D, int group, bool fp8, int mode,
                               hipStream_t stream);
+hipError_t launch_decode_stream(const DecodeArgs& a, int B, int D, int group, bool fp8, int mode,
+                                hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int B, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int T, int D, bool fused, hipStream_t stream);
 

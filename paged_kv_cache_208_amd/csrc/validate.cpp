@@ -135,14 +135,21 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
                                  const float* part_out, const float* part_max,
                                  const float* part_sum, const uint32_t* counters,
                                  int max_partitions) {
-  // the attention part is checked exactly as paged_attn_decode checks it
+  // the attention part is checked as paged_attn_decode checks partitioned work
+  // (partition_size 0 here means a balanced split, which needs the same workspace)
+  const int ps_check = partition_size == 0 ? BS : partition_size;
   int st = pkv_validate_decode(out, q, k_pool, v_pool, k_scale, v_scale, block_tables,
-                               context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale, kv_dtype,
-                               partition_size, part_out, part_max, part_sum, max_partitions);
+                               context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale, kv_dtype, ps_check,
+                               part_out, part_max, part_sum,
+                               partition_size == 0 ? MBS : max_partitions);
   if (st != PKV_OK || B == 0) return st;
   if (!out || !aligned(out, 16)) return PKV_EINVAL;
-  if (partition_size != 0) {
-    if (!counters || !aligned(counters, 4)) return PKV_EINVAL;
+  if (!counters || !aligned(counters, 4)) return PKV_EINVAL;
+  if (partition_size == 0) {
+    // balanced split: between 3 and 64 pieces per sequence
+    if (max_partitions < 3) return PKV_EINVAL;
+    if (max_partitions > pkv::kMaxStepPartitions) return PKV_EUNSUPPORTED;
+  } else {
     // the in-kernel combine holds at most 64 partitions per sequence
     if ((int64_t(MBS) * BS + partition_size - 1) / partition_size > pkv::kMaxStepPartitions)
       return PKV_EUNSUPPORTED;

@@ -179,7 +179,11 @@ def _step_args(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     ({}, 0),
-    (dict(partition_size=0, counters=None, part_out=None, part_max=None, part_sum=None), 0),
+    (dict(partition_size=0, max_partitions=16), 0),
+    (dict(partition_size=0, max_partitions=2), -1),
+    (dict(partition_size=0, max_partitions=65), -2),
+    (dict(partition_size=0, part_out=None), -1),
+    (dict(partition_size=0, counters=None), -1),
     (dict(B=0, out=None), 0),
     (dict(out=None), -1),
     (dict(counters=None), -1),

@@ -23,13 +23,12 @@ def _u16(x):
     return np.ascontiguousarray(x).view(np.uint16)
 
 
-def _step(cfg, g, ps, *, append=True, qknorm=False):
+def _step(cfg, g, ps, *, append=True, qknorm=False, splits=16):
+    """ps > 0: fixed partitions; ps == 0: balanced split into <= splits pieces."""
     B, Hq, D = g["q"].shape
     out = torch.full((B, Hq, D), float("nan"), dtype=torch.float16, device="cuda")
-    ws = None
-    if ps:
-        P = _lib.max_partitions_for(cfg.mbs, ps)
-        ws = _lib.alloc_step_workspace(B, Hq, cfg.Hkv, D, P)
+    P = _lib.max_partitions_for(cfg.mbs, ps) if ps else splits
+    ws = _lib.alloc_step_workspace(B, Hq, cfg.Hkv, D, P)
     kw = {}
     if append:
         kw.update(k_new=g["k_new"], v_new=g["v_new"])
@@ -42,18 +41,17 @@ def _step(cfg, g, ps, *, append=True, qknorm=False):
     return out, ws
 
 
-@pytest.mark.parametrize("ps", [0, 16, 64, 512])
-def test_step_plain_append(ps):
+@pytest.mark.parametrize("ps,splits", [(0, 3), (0, 16), (0, 64), (16, 0), (64, 0), (512, 0)])
+def test_step_plain_append(ps, splits):
     cfg, d = batch("c2", B=6, len_lo=1, len_hi=700, mbs=44)
     g = to_device(d)
-    out, ws = _step(cfg, g, ps)
+    out, ws = _step(cfg, g, ps, splits=splits)
     kp, vp = append_ref(d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], d["slot_mapping"])
     assert np.array_equal(_u16(g["k_pool"].cpu().numpy()), _u16(kp))
     assert np.array_equal(_u16(g["v_pool"].cpu().numpy()), _u16(vp))
     ref = attn_ref(d["q"], kp, vp, d["block_tables"], d["context_lens"], cfg.scale)
     assert max_abs(out, ref) <= TOL_F16
-    if ws is not None:
-        assert torch.count_nonzero(ws[3]).item() == 0, "arrival counters not reset"
+    assert torch.count_nonzero(ws[3]).item() == 0, "arrival counters not reset"
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -82,8 +80,7 @@ def test_step_qknorm(D, ps):
     assert np.all(dk <= ulpk.astype(np.float64))
     ref = attn_ref(q2, kp, vp, d["block_tables"], d["context_lens"], cfg.scale)
     assert max_abs(out, ref) <= TOL_F16
-    if ws is not None:
-        assert torch.count_nonzero(ws[3]).item() == 0
+    assert torch.count_nonzero(ws[3]).item() == 0
 
 
 @pytest.mark.parametrize("ps", [0, 64, 512])
@@ -102,11 +99,9 @@ def test_step_repeats_bitwise_and_matches_three_calls():
     rounding of the final division."""
     cfg, d = batch("c2", B=5, len_lo=1, len_hi=700, mbs=44)
     g = to_device(d)
-    ps = 64
-    P = _lib.max_partitions_for(cfg.mbs, ps)
-    ws = _lib.alloc_step_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.D, P)
+    ws = _lib.alloc_step_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.D, 16)
     outs = []
-    for _ in range(3):
+    for ps in (0, 0, 0):
         out = torch.empty_like(g["q"])
         _lib.paged_decode_step(out, g["q"], g["k_pool"], g["v_pool"], g["block_tables"],
                                g["context_lens"], cfg.scale, k_new=g["k_new"], v_new=g["v_new"],
@@ -119,13 +114,14 @@ def test_step_repeats_bitwise_and_matches_three_calls():
     _lib.paged_kv_append(g2["k_new"], g2["v_new"], g2["k_pool"], g2["v_pool"], g2["slot_mapping"])
     ref = torch.empty_like(g2["q"])
     _lib.decode_step(ref, g2["q"], g2["k_pool"], g2["v_pool"], g2["block_tables"],
-                     g2["context_lens"], cfg.scale, partition_size=ps)
+                     g2["context_lens"], cfg.scale, partition_size=64)
     torch.cuda.synchronize()
     diff = (outs[0].double() - ref.double()).abs().max().item()
     assert diff <= 2e-3
 
 
-def test_step_empty_and_single_token_contexts():
+@pytest.mark.parametrize("ps", [0, 64])
+def test_step_empty_and_single_token_contexts(ps):
     cfg, d = batch("c2", B=5, len_lo=1, len_hi=300, mbs=19)
     lens = d["context_lens"].copy()
     lens[0] = 0
@@ -136,7 +132,7 @@ def test_step_empty_and_single_token_contexts():
     slots[3] = int(tab[3, 0]) * 16
     d2 = dict(d, context_lens=lens, slot_mapping=slots)
     g = to_device(d2)
-    out, ws = _step(cfg, g, 64)
+    out, ws = _step(cfg, g, ps)
     kp, vp = append_ref(d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], slots)
     assert np.array_equal(_u16(g["k_pool"].cpu().numpy()), _u16(kp))
     assert torch.all(out[0] == 0)
@@ -148,12 +144,14 @@ def test_step_empty_and_single_token_contexts():
     assert torch.count_nonzero(ws[3]).item() == 0
 
 
-@pytest.mark.parametrize("name", ["c2", "c4", "c5"])
-def test_step_full_size_sampled(name):
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("balanced", [True, False])
+def test_step_full_size_sampled(name, balanced):
     cfg, d = batch(name)
     g = to_device(d)
     fp8 = cfg.kv_dtype == "e4m3"
-    out, ws = _step(cfg, g, cfg.partition_size, append=not fp8, qknorm=cfg.fused_append)
+    out, ws = _step(cfg, g, 0 if balanced else cfg.partition_size, append=not fp8,
+                    qknorm=cfg.fused_append)
     o = out.cpu().double().numpy()
     assert np.all(np.isfinite(o))
     seqs = sample_seqs(cfg.B, 5, seed=3)
