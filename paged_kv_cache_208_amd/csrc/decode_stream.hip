@@ -20,19 +20,39 @@
 // Partials and arrival counters use device-scope coherent accesses; the
 // counters return to zero.
 //
+// Inside the loop a wave issues only loads (KV tiles, and q when a tile
+// starts a segment): vector memory operations complete in issue order, so a
+// store would hold up the wait for every tile behind it.  The step's new rows
+// are therefore written before the loop (by the wave whose range holds the
+// segment's last tile), and a partial that ends mid-range stays in LDS until
+// the range is done.  Block ids and lengths come through the scalar cache.
+//
 // Each wave is its own 64-thread workgroup; the tile engine is the MFMA one
 // of decode_tile.h.
 #include "decode_tile.h"
 #include "shape_limits.h"
 
-// Waves resident per SIMD (the register budget follows from it); the grid is
-// one wave per resident slot, four SIMDs per CU.
-#ifndef PKV_STREAM_WAVES_PER_EU
-#define PKV_STREAM_WAVES_PER_EU 2
+// Waves resident per SIMD, which sets the register budget; the grid is one
+// wave per resident slot, four SIMDs per CU.  fp16 tiles (8 KiB of K and V)
+// keep enough bytes in flight with one wave per SIMD and its full register
+// file; E4M3 tiles are half the size and want two.
+#ifndef PKV_STREAM_WAVES_PER_EU_F16
+#define PKV_STREAM_WAVES_PER_EU_F16 1
+#endif
+#ifndef PKV_STREAM_WAVES_PER_EU_FP8
+#define PKV_STREAM_WAVES_PER_EU_FP8 2
+#endif
+#ifndef PKV_STREAM_DEPTH
+#define PKV_STREAM_DEPTH 2
 #endif
 
 namespace pkv {
 namespace {
+
+template <bool FP8>
+constexpr int stream_waves_per_eu() {
+  return FP8 ? PKV_STREAM_WAVES_PER_EU_FP8 : PKV_STREAM_WAVES_PER_EU_F16;
+}
 
 // Position of one tile in the flattened order.
 struct Cursor {
@@ -58,17 +78,26 @@ __device__ __forceinline__ int64_t wave_scan(int64_t x) {
   return x;
 }
 
-// Total tiles of the batch (all kv heads).
-__device__ __forceinline__ int64_t total_tiles(const DecodeArgs& a, int B) {
+// Tiles of the batch (all kv heads) and the most tiles of one sequence.
+struct Totals {
+  int64_t tiles;
+  int max_tiles;
+};
+
+__device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t tot = 0;
+  int mx = 0;
   for (int c = 0; c < B; c += kWave) {
     const int b = c + lane;
-    const int L = b < B ? a.context_lens[b] : 0;
-    const int64_t incl = wave_scan(int64_t((L + 15) / 16));
+    const int T = b < B ? (a.context_lens[b] + 15) / 16 : 0;
+    const int64_t incl = wave_scan(int64_t(T));
     tot += readlane64(incl, kWave - 1);
+    mx = max(mx, T);
   }
-  return tot * a.Hkv;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) mx = max(mx, __shfl_xor(mx, off));
+  return Totals{tot * a.Hkv, __builtin_amdgcn_readfirstlane(mx)};
 }
 
 // Cursor of flattened tile t (t < total).
@@ -117,6 +146,7 @@ __device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B) {
 struct Meta {
   int b, kvh, n, L, T;
   int id;      // physical block of the tile
+  int slot;    // angle table of the segment (QK-norm modes)
   int64_t S;
   bool first;  // first tile of the wave's piece of the segment
   bool last;   // last tile of the wave's piece of the segment
@@ -127,6 +157,7 @@ __device__ __forceinline__ Meta meta_of(const Cursor& c, const DecodeArgs& a, in
   Meta m;
   // a scalar load; its result is first needed one loop step later
   m.id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + c.n);
+  m.slot = 0;
   m.b = c.b;
   m.kvh = c.kvh;
   m.n = c.n;
@@ -143,119 +174,144 @@ struct StreamKernel {
   using Geo = MfmaGeo<D, FP8>;
   static constexpr bool APPEND = (MODE & kModeAppend) != 0;
   static constexpr bool QKNORM = (MODE & kModeQkNorm) != 0;
+  // tiles in the load pipeline of a wave
+  static constexpr int kDepth = PKV_STREAM_DEPTH;
 
-  // q of head slot n16 of the segment's group (QK-norm applied when asked),
-  // as the B operand of the QK products; zero past the group.
+  // q of head slot n16 of the segment's group, laid out as the B operand of
+  // the QK products; zero past the group.  Slots past the group read outside
+  // the buffer's bound, which returns zeros, so no lane overwrites a register
+  // that a load is still filling.  QK-norm is applied when the segment's
+  // first tile is computed, once the loads have landed.
   static __device__ __forceinline__ void load_q(half8_t* qop, const DecodeArgs& a, int b, int kvh,
-                                                int g, int n16, const float* s_cos,
-                                                const float* s_sin) {
-    const _Float16* qh =
-        static_cast<const _Float16*>(a.q) + (size_t(b) * a.Hq + kvh * G + min(n16, G - 1)) * D;
+                                                int g, int n16) {
+    const _Float16* qg = static_cast<const _Float16*>(a.q) + (size_t(b) * a.Hq + kvh * G) * D;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(qg, G * D * int(sizeof(_Float16)));
+    const int row = n16 < G ? n16 * D : G * D;
 #pragma unroll
     for (int c = 0; c < Geo::kQK; ++c)
-      qop[c] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(qh + qk_dim0<FP8>(c, g)));
-    if constexpr (QKNORM) norm_rope_chunks<D>(qop, a.gamma_q, a.eps, s_cos, s_sin, g);
-    if (n16 >= G)
-#pragma unroll
-      for (int c = 0; c < Geo::kQK; ++c) qop[c] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      qop[c] = __builtin_bit_cast(half8_t, buffer_load16(r, (row + qk_dim0<FP8>(c, g)) * int(sizeof(_Float16))));
   }
 
-  // Write the step's new row (token L-1) of segment m into the tile about to
-  // be read, from the lanes that will load each piece (same lane, same
-  // address, program order: the loads observe the stores).
-  static __device__ __forceinline__ void append_row(const DecodeArgs& a, const Meta& m, size_t base,
-                                                    int g, int n16, int k_off, int v_off,
-                                                    const float* s_cos, const float* s_sin) {
-    const int r_new = (m.L - 1) % 16;
-    const size_t row = size_t(m.b) * a.Hkv + m.kvh;
-    const _Float16* kn = static_cast<const _Float16*>(a.k_new) + row * D;
-    const _Float16* vn = static_cast<const _Float16*>(a.v_new) + row * D;
-    half8_t kc[Geo::kKLoads];
-#pragma unroll
-    for (int i = 0; i < Geo::kKLoads; ++i)
-      kc[i] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(kn + (4 * i + g) * 8));
-    if constexpr (QKNORM) norm_rope_chunks<D>(kc, a.gamma_k, a.eps, s_cos, s_sin, g);
-    uint8_t* kt = const_cast<uint8_t*>(a.k_pool) + base;
-    uint8_t* vt = const_cast<uint8_t*>(a.v_pool) + base;
-    if (n16 == r_new)
+  // Write the step's new k and v row (token L-1) of every segment whose last
+  // tile lies in the range [t0, t1), before any tile of the range is loaded.
+  // The lanes that store each piece are the ones that later load it (same
+  // lane, same address, program order: the loads observe the stores).  The
+  // loop then carries no append work.  c is the cursor of tile t0; s_cos /
+  // s_sin hold scratch angle tables (QK-norm).
+  static __device__ __forceinline__ void append_rows(const DecodeArgs& a, int B, Cursor c, int64_t t1,
+                                                     int g, int n16, int k_off, int v_off, float* s_cos,
+                                                     float* s_sin, const double* s_f,
+                                                     const float* s_gk) {
+    using VW = typename Words<Geo::kVWords>::T;
+    while (c.S + c.T - 1 < t1) {
+      const int id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + (c.T - 1));
+      const size_t row = size_t(c.b) * a.Hkv + c.kvh;
+      const _Float16* kn = static_cast<const _Float16*>(a.k_new) + row * D;
+      const _Float16* vn = static_cast<const _Float16*>(a.v_new) + row * D;
+      half8_t kc[Geo::kKLoads];
 #pragma unroll
       for (int i = 0; i < Geo::kKLoads; ++i)
-        *reinterpret_cast<u32x4*>(kt + k_off + i * 64) = __builtin_bit_cast(u32x4, kc[i]);
-    if (g == r_new / 4) {
-      using VW = typename Words<Geo::kVWords>::T;
-      *reinterpret_cast<VW*>(vt + v_off + (r_new % 4) * Geo::kRow) =
-          *reinterpret_cast<const VW*>(vn + n16 * (D / 16));
+        kc[i] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(kn + (4 * i + g) * 8));
+      const VW vc = *reinterpret_cast<const VW*>(vn + n16 * (D / 16));
+      if constexpr (QKNORM) {
+        rope_angles<D>(s_f, s_cos, s_sin, c.L - 1);
+        norm_rope_chunks<D>(kc, s_gk, a.eps, s_cos, s_sin, g);
+      }
+      const int r_new = (c.L - 1) % 16;
+      const size_t base = (size_t(id) * a.Hkv + c.kvh) * Geo::kTile;
+      uint8_t* kt = const_cast<uint8_t*>(a.k_pool) + base;
+      uint8_t* vt = const_cast<uint8_t*>(a.v_pool) + base;
+      if (n16 == r_new)
+#pragma unroll
+        for (int i = 0; i < Geo::kKLoads; ++i)
+          *reinterpret_cast<u32x4*>(kt + k_off + i * 64) = __builtin_bit_cast(u32x4, kc[i]);
+      if (g == r_new / 4) *reinterpret_cast<VW*>(vt + v_off + (r_new % 4) * Geo::kRow) = vc;
+      // on to the next segment
+      c.n = c.T - 1;
+      advance(c, a, B);
+      if (c.b >= B) break;
     }
   }
 
-  // Issue the loads of tile m (writing the new row first when this is its
-  // segment's last tile).  A tile that is not live issues the same loads with
-  // no valid rows: they read nothing, but every loop step then has the same
-  // number of loads in flight behind the tile being computed, so the wait
-  // before the products stays partial on every path.
+  // Issue the loads of tile m.  A tile that is not live issues the same
+  // loads with no valid rows: they read nothing, but every loop step then has
+  // the same number of loads in flight behind the tile being computed, so the
+  // wait before the products stays partial on every path.
   static __device__ __forceinline__ void issue(MTile<D, FP8>& t, const DecodeArgs& a, const Meta& m,
-                                               bool live, int g, int n16, int k_off, int v_off,
-                                               const float* s_cos, const float* s_sin) {
+                                               bool live, int k_off, int v_off) {
     const size_t base = live ? (size_t(m.id) * a.Hkv + m.kvh) * Geo::kTile : 0;
-    if constexpr (APPEND)
-      if (live && m.n == m.T - 1) append_row(a, m, base, g, n16, k_off, v_off, s_cos, s_sin);
     load_mtile_at<D, FP8>(t, a, base, live ? min(16, m.L - 16 * m.n) : 0, k_off, v_off);
   }
 
-  // End of the wave's piece of segment m: write the output directly, or a
-  // partial that the last arriving piece combines.
-  static __device__ __forceinline__ void flush(MState<D, FP8>& st, const DecodeArgs& a, const Meta& m,
-                                               const half8_t* qop, int64_t tpw, int worker, int g,
-                                               int n16, float* s_w) {
-    const float l = group4_sum(st.l);
-    const int64_t j0 = m.S / tpw;
-    const int pieces = int((m.S + m.T - 1) / tpw - j0 + 1);
-    const size_t row0 = size_t(m.b) * a.Hq + m.kvh * G;
-    bool finisher = pieces == 1;
-    if (pieces == 1) {
-      if (n16 < G) {
-        const float inv = 1.0f / l;
-        _Float16* o = static_cast<_Float16*>(a.out) + (row0 + n16) * D;
+  // Pieces the wave ranges cut segment m into (tpw tiles per range).
+  static __device__ __forceinline__ int pieces_of(const Meta& m, int64_t tpw) {
+    return int((m.S + m.T - 1) / tpw - m.S / tpw + 1);
+  }
+
+  // Output rows of a segment that lies inside one wave's range: o / l.
+  static __device__ __forceinline__ void store_direct(const MState<D, FP8>& st, float l,
+                                                      const DecodeArgs& a, int seg, int g, int n16) {
+    if (n16 >= G) return;
+    const float inv = 1.0f / l;
+    _Float16* o = static_cast<_Float16*>(a.out) + (size_t(seg) * G + n16) * D;
+    typedef _Float16 hv __attribute__((ext_vector_type(Geo::kPV)));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          _Float16 h[Geo::kPV];
+    for (int r = 0; r < 4; ++r) {
+      hv v;
 #pragma unroll
-          for (int i = 0; i < Geo::kPV; ++i) h[i] = (_Float16)(st.acc[i][r] * inv);
-          typedef _Float16 hv __attribute__((ext_vector_type(Geo::kPV)));
-          hv v;
-#pragma unroll
-          for (int i = 0; i < Geo::kPV; ++i) v[i] = h[i];
-          *reinterpret_cast<hv*>(o + (4 * g + r) * Geo::kPV) = v;
-        }
-      }
-    } else {
-      store_partial(st, l, a, row0, int(worker - j0), g, n16, s_w);
-      __builtin_amdgcn_s_waitcnt(0);  // the partial has reached device scope
-      uint32_t* ctr = a.counters + size_t(m.b) * a.Hkv + m.kvh;
-      uint32_t prev = 0;
-      if ((threadIdx.x & (kWave - 1)) == 0)
-        prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      prev = __builtin_amdgcn_readfirstlane(prev);
-      if (prev == uint32_t(pieces - 1)) {
-        combine(a, row0, pieces, s_w);
-        if ((threadIdx.x & (kWave - 1)) == 0)
-          __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        finisher = true;
-      }
+      for (int i = 0; i < Geo::kPV; ++i) v[i] = (_Float16)(st.acc[i][r] * inv);
+      *reinterpret_cast<hv*>(o + (4 * g + r) * Geo::kPV) = v;
     }
-    if constexpr (QKNORM) {
-      // q' goes back in place once no other wave of the segment needs q
-      if (finisher && n16 < G) {
-        _Float16* qh = const_cast<_Float16*>(static_cast<const _Float16*>(a.q)) + (row0 + n16) * D;
-#pragma unroll
-        for (int c = 0; c < Geo::kQK; ++c)
-          *reinterpret_cast<u32x4*>(qh + qk_dim0<false>(c, g)) = __builtin_bit_cast(u32x4, qop[c]);
-      }
-    }
+  }
+
+  static __device__ __forceinline__ void reset(MState<D, FP8>& st) {
     st.m = -FLT_MAX;
     st.l = 0.0f;
 #pragma unroll
     for (int i = 0; i < Geo::kPV; ++i) st.acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // q' (QK-norm) back in place, from the operand registers or from the LDS
+  // copy taken when the piece ended; done by the wave that finishes the
+  // segment, when no other wave still needs q.
+  static __device__ __forceinline__ void write_q(const DecodeArgs& a, int seg, const half8_t* qop,
+                                                 int g, int n16) {
+    if (n16 >= G) return;
+    _Float16* qh = const_cast<_Float16*>(static_cast<const _Float16*>(a.q)) + (size_t(seg) * G + n16) * D;
+#pragma unroll
+    for (int c = 0; c < Geo::kQK; ++c)
+      *reinterpret_cast<u32x4*>(qh + qk_dim0<false>(c, g)) = __builtin_bit_cast(u32x4, qop[c]);
+  }
+  static __device__ __forceinline__ void stash_q(_Float16* s_q, const half8_t* qop, int g, int n16) {
+    if (n16 >= G) return;
+#pragma unroll
+    for (int c = 0; c < Geo::kQK; ++c)
+      *reinterpret_cast<u32x4*>(s_q + n16 * D + qk_dim0<false>(c, g)) = __builtin_bit_cast(u32x4, qop[c]);
+  }
+  static __device__ __forceinline__ void write_q_stashed(const DecodeArgs& a, int seg,
+                                                         const _Float16* s_q, int g, int n16) {
+    half8_t q[Geo::kQK];
+#pragma unroll
+    for (int c = 0; c < Geo::kQK; ++c)
+      q[c] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(s_q + min(n16, G - 1) * D +
+                                                                         qk_dim0<false>(c, g)));
+    write_q(a, seg, q, g, n16);
+  }
+
+  // Count this piece's arrival at its segment (the partial must already be at
+  // device scope); returns the previous count in lane 0.
+  static __device__ __forceinline__ uint32_t arrive(const DecodeArgs& a, int seg) {
+    uint32_t prev = 0;
+    if ((threadIdx.x & (kWave - 1)) == 0)
+      prev = __hip_atomic_fetch_add(a.counters + seg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return prev;
+  }
+
+  // The last piece to arrive combines the partials and re-arms the counter.
+  static __device__ __forceinline__ void finish(const DecodeArgs& a, int seg, int pieces, float* s_w) {
+    combine(a, size_t(seg) * G, pieces, s_w);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+      __hip_atomic_store(a.counters + seg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // Float4 pieces of one partial (G rows of D) and how many each lane owns.
@@ -273,21 +329,29 @@ struct StreamKernel {
                sizeof(float));
   }
 
-  // Piece j of the segment at output row row0: o / l, max (natural-log
-  // units) and l.  The normalised rows go through LDS so each lane writes
-  // whole 16-byte pieces of them.
-  static __device__ __forceinline__ void store_partial(const MState<D, FP8>& st, float l,
-                                                       const DecodeArgs& a, size_t row0, int j, int g,
+  // A piece's partial, kept in LDS until it is written out: o / l of the G
+  // rows (G * D floats), then the G maxima (natural-log units) and G sums.
+  static constexpr int kStage = G * D + 2 * G;
+
+  static __device__ __forceinline__ void stage_partial(const MState<D, FP8>& st, float l, int g,
                                                        int n16, float* s_o) {
-    static_assert(D <= 2 * kMaxStepPartitions, "staging fits the weights' LDS");
-    const int lane = threadIdx.x & (kWave - 1);
-    if (n16 < G) {
-      const float inv = 1.0f / l;
+    if (n16 >= G) return;
+    const float inv = 1.0f / l;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int i = 0; i < Geo::kPV; ++i) s_o[n16 * D + (4 * g + r) * Geo::kPV + i] = st.acc[i][r] * inv;
+      for (int i = 0; i < Geo::kPV; ++i) s_o[n16 * D + (4 * g + r) * Geo::kPV + i] = st.acc[i][r] * inv;
+    if (g == 0) {
+      s_o[G * D + n16] = st.m * kLn2;
+      s_o[G * D + G + n16] = l;
     }
+  }
+
+  // Piece j of the segment at output row row0, from its LDS copy: each lane
+  // writes whole 16-byte pieces of the rows, with device-scope coherence.
+  static __device__ __forceinline__ void write_partial(const DecodeArgs& a, size_t row0, int j,
+                                                       const float* s_o) {
+    const int lane = threadIdx.x & (kWave - 1);
     const __amdgpu_buffer_rsrc_t rs = partial_rows(a, row0);
 #pragma unroll
     for (int k = 0; k < kOwn; ++k) {
@@ -295,10 +359,10 @@ struct StreamKernel {
       if (c < kF4)
         store16_coherent(rs, partial_offset(a, c, j), *reinterpret_cast<const u32x4*>(s_o + 4 * c));
     }
-    if (g == 0 && n16 < G) {
-      const size_t pr = (row0 + n16) * a.max_partitions + j;
-      store_f32<true>(a.part_max + pr, st.m * kLn2);
-      store_f32<true>(a.part_sum + pr, l);
+    if (lane < G) {
+      const size_t pr = (row0 + lane) * a.max_partitions + j;
+      store_f32<true>(a.part_max + pr, s_o[G * D + lane]);
+      store_f32<true>(a.part_sum + pr, s_o[G * D + G + lane]);
     }
   }
 
@@ -328,7 +392,7 @@ struct StreamKernel {
       w[0] = den;
     }
     __builtin_amdgcn_s_waitcnt(0);
-    constexpr int kBatch = kOwn >= 4 ? 1 : 4 / kOwn;
+    constexpr int kBatch = kOwn >= 16 ? 1 : 16 / kOwn;
     const __amdgpu_buffer_rsrc_t rs = partial_rows(a, row0);
     float4_t num[kOwn];
 #pragma unroll
@@ -370,7 +434,7 @@ struct StreamKernel {
 };
 
 template <int D, int G, bool FP8, int MODE>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PKV_STREAM_WAVES_PER_EU, 8)))
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<FP8>(), 8)))
 void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   using K = StreamKernel<D, G, FP8, MODE>;
   using Geo = MfmaGeo<D, FP8>;
@@ -382,73 +446,186 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   const int k_off = n16 * Geo::kRow + g * 16;
   const int v_off = (4 * g) * Geo::kRow + n16 * Geo::kVBytes;
 
-  __shared__ float s_w[2 * G * kMaxStepPartitions];
-  __shared__ float s_cos[K::QKNORM ? D / 2 : 1];
-  __shared__ float s_sin[K::QKNORM ? D / 2 : 1];
+  __shared__ float s_w[2 * G * kMaxStepPartitions];  // combine weights
+  __shared__ float s_fin[K::kStage];                  // the range's last piece
+  __shared__ float s_pend[K::kStage];                 // a piece that ended earlier
+  // rotation angles of two segments' positions: the segment being computed
+  // and the next one being prepared (QK-norm modes)
+  __shared__ float s_cos[K::QKNORM ? 2 * (D / 2) : 1];
+  __shared__ float s_sin[K::QKNORM ? 2 * (D / 2) : 1];
+  __shared__ _Float16 s_q[K::QKNORM ? G * D : 1];
+  __shared__ double s_f[K::QKNORM ? D / 2 : 1];      // rotation frequencies
+  __shared__ float s_gq[K::QKNORM ? D : 1];          // RMSNorm weights of q and k
+  __shared__ float s_gk[K::QKNORM ? D : 1];
 
-  const int64_t W = total_tiles(a, B);
-  // equal shares, but long enough that a segment spans at most max_partitions
+  const Totals tot = total_tiles(a, B);
+  const int64_t W = tot.tiles;
+  // equal shares, but long enough that no sequence's segment is cut into more
+  // than max_partitions pieces: T tiles span at most (T-1)/tpw + 2 ranges
   const int64_t tpw = max((W + workers - 1) / workers,
-                          int64_t(a.MBS + a.max_partitions - 3) / (a.max_partitions - 2));
+                          int64_t(tot.max_tiles + a.max_partitions - 3) / (a.max_partitions - 2));
   const int64_t t0 = int64_t(worker) * tpw;
   const int64_t t1 = min(W, t0 + tpw);
 
   if (t0 < t1) {
     Cursor cur = locate(a, B, t0);
-    int rope_b = -1;  // sequence whose angles are in s_cos / s_sin
-    auto prepare_segment = [&](const Meta& m, half8_t* qdst) {
+    int rope_b[2] = {-1, -1};  // sequence whose angles are in each table
+    int ord = 0;                // segments entered so far; parity picks the table
+    if constexpr (K::QKNORM) {
+      rope_freqs<D>(s_f, a.theta);
+      for (int i = lane; i < D; i += kWave) {
+        s_gq[i] = a.gamma_q[i];
+        s_gk[i] = a.gamma_k[i];
+      }
+    }
+    if constexpr (K::APPEND)
+      K::append_rows(a, B, cur, t1, g, n16, k_off, v_off, s_cos, s_sin, s_f, s_gk);
+    auto prepare_segment = [&](Meta& m) {
+      m.slot = ord++ & 1;
       if constexpr (K::QKNORM) {
-        if (m.b != rope_b) {
-          rope_table<D, 1>(s_cos, s_sin, m.L - 1, a.theta);
-          rope_b = m.b;
+        if (m.b != rope_b[m.slot]) {
+          rope_angles<D>(s_f, s_cos + m.slot * (D / 2), s_sin + m.slot * (D / 2), m.L - 1);
+          rope_b[m.slot] = m.b;
         }
       }
-      K::load_q(qdst, a, m.b, m.kvh, g, n16, s_cos, s_sin);
     };
 
     MState<D, FP8> st;
-    st.m = -FLT_MAX;
-    st.l = 0.0f;
-#pragma unroll
-    for (int i = 0; i < Geo::kPV; ++i) st.acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    K::reset(st);
 
-    half8_t qop[Geo::kQK], qnext[Geo::kQK];
-    MTile<D, FP8> ta, tb;
-    // metas run one tile ahead of the data loads: `ahead` is the tile after
-    // the one being loaded, so its block id has a whole step to arrive
-    Meta ma = meta_of(cur, a, t0, t0, t1), mb, ahead;
-    if (t0 + 1 < t1) {
-      advance(cur, a, B);
-      ahead = meta_of(cur, a, t0 + 1, t0, t1);
+    // NB tile buffers: while tile t is computed, tiles t+1 .. t+NB-1 are in
+    // flight.  Metas run one tile further ahead (`ahead`), so each block id
+    // has a whole step to arrive.
+    constexpr int NB = K::kDepth;
+    MTile<D, FP8> tl[NB];
+    Meta mt[NB];
+    Meta ahead;
+    Meta mfin;          // the range's last tile
+    int last_slot = 0;  // angle table of the most recently issued tile
+    // q of the segment of the tile being computed (qop), and of the segments
+    // that start at the tiles in flight: a tile that starts a segment loads
+    // its q into the buffer of its own slot, just before its K and V, and the
+    // buffer moves into qop when the tile is computed.
+    half8_t qop[Geo::kQK];
+    half8_t qbuf[NB][Geo::kQK];
+    auto take = [&](Meta& m, half8_t* qdst) {
+      if (m.first) {
+        prepare_segment(m);
+        K::load_q(qdst, a, m.b, m.kvh, g, n16);
+      } else {
+        m.slot = last_slot;
+      }
+      last_slot = m.slot;
+    };
+    mt[0] = meta_of(cur, a, t0, t0, t1);
+    mt[0].first = true;  // the range starts with a piece of a segment
+    take(mt[0], qbuf[0]);
+    K::issue(tl[0], a, mt[0], true, k_off, v_off);
+#pragma unroll
+    for (int k = 1; k < NB; ++k) {
+      const bool live = t0 + k < t1;
+      if (live) {
+        advance(cur, a, B);
+        Meta m = meta_of(cur, a, t0 + k, t0, t1);
+        if (k < NB - 1) {
+          mt[k] = m;
+          take(mt[k], qbuf[k]);
+        } else {
+          ahead = m;
+        }
+      }
+      if (k < NB - 1) K::issue(tl[k], a, mt[k], live, k_off, v_off);
     }
-    prepare_segment(ma, qnext);
-    K::issue(ta, a, ma, true, g, n16, k_off, v_off, s_cos, s_sin);
 
-    // process tile X (meta mx), loading the tile after it into Y
-    auto step = [&](MTile<D, FP8>& x, const Meta& mx, MTile<D, FP8>& y, Meta& my, int64_t t) {
-      if (mx.first)
-#pragma unroll
-        for (int c = 0; c < Geo::kQK; ++c) qop[c] = qnext[c];
-      const bool live = t + 1 < t1;
+    // A shared segment whose piece ends before the range does (only the
+    // range's first segment can) keeps its partial in LDS until the range is
+    // done.  Stores issued inside the loop would hold up the waits for the
+    // tiles behind them (vector memory operations complete in order), and
+    // the segment's last pieces end with the ranges anyway.
+    bool pend = false;
+    int pseg = 0, ppieces = 0, pj = 0;
+
+    // compute tile t (X, meta mx, q buffer qx); load tile t+NB-1 into Y
+    // (meta my, q buffer qy)
+    auto step = [&](MTile<D, FP8>& x, const Meta& mx, const half8_t* qx, MTile<D, FP8>& y, Meta& my,
+                    half8_t* qy, int64_t t) {
+      const bool live = t + NB - 1 < t1;
       if (live) {
         my = ahead;
-        if (my.first) prepare_segment(my, qnext);
+        take(my, qy);
       }
-      K::issue(y, a, my, live, g, n16, k_off, v_off, s_cos, s_sin);
-      if (t + 2 < t1) {
+      K::issue(y, a, my, live, k_off, v_off);
+      if (t + NB < t1) {
         advance(cur, a, B);
-        ahead = meta_of(cur, a, t + 2, t0, t1);
+        ahead = meta_of(cur, a, t + NB, t0, t1);
+      }
+      issue_fence();  // Y's loads stay ahead of the waits below
+      if (mx.first) {
+#pragma unroll
+        for (int c = 0; c < Geo::kQK; ++c) qop[c] = qx[c];
+        if constexpr (K::QKNORM)
+          norm_rope_chunks<D>(qop, s_gq, a.eps, s_cos + mx.slot * (D / 2),
+                              s_sin + mx.slot * (D / 2), g);
       }
       issue_fence();
       mfma_tile<D, FP8>(st, x, qop, a.scale_log2, g);
-      if (mx.last) K::flush(st, a, mx, qop, tpw, worker, g, n16, s_w);
+      if (t + 1 >= t1) {
+        mfin = mx;
+        return;
+      }
+      if (mx.last) {
+        const int pieces = K::pieces_of(mx, tpw);
+        const int seg = mx.b * a.Hkv + mx.kvh;
+        const float l = group4_sum(st.l);
+        if (pieces == 1) {
+          K::store_direct(st, l, a, seg, g, n16);
+          if constexpr (K::QKNORM) K::write_q(a, seg, qop, g, n16);
+        } else {
+          K::stage_partial(st, l, g, n16, s_pend);
+          if constexpr (K::QKNORM) K::stash_q(s_q, qop, g, n16);
+          pend = true;
+          pseg = seg;
+          ppieces = pieces;
+          pj = int(worker - mx.S / tpw);
+        }
+        K::reset(st);
+      }
     };
 
     for (int64_t t = t0; t < t1;) {
-      step(ta, ma, tb, mb, t);
-      if (++t >= t1) break;
-      step(tb, mb, ta, ma, t);
-      ++t;
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int v = (u + NB - 1) % NB;
+        step(tl[u], mt[u], qbuf[u], tl[v], mt[v], qbuf[v], t);
+        if (++t >= t1) break;
+      }
+    }
+
+    // the range's last piece
+    const Meta& mf = mfin;
+    const int fpieces = K::pieces_of(mf, tpw);
+    const int fseg = mf.b * a.Hkv + mf.kvh;
+    const float l = group4_sum(st.l);
+    if (fpieces == 1) {
+      K::store_direct(st, l, a, fseg, g, n16);
+      if constexpr (K::QKNORM) K::write_q(a, fseg, qop, g, n16);
+    } else {
+      K::stage_partial(st, l, g, n16, s_fin);
+      K::write_partial(a, size_t(fseg) * G, int(worker - mf.S / tpw), s_fin);
+    }
+    if (pend) K::write_partial(a, size_t(pseg) * G, pj, s_pend);
+    if (pend || fpieces > 1) {
+      __builtin_amdgcn_s_waitcnt(0);  // partials at device scope
+      const uint32_t pprev = pend ? K::arrive(a, pseg) : 0u;
+      const uint32_t fprev = fpieces > 1 ? K::arrive(a, fseg) : 0u;
+      if (pend && __builtin_amdgcn_readfirstlane(pprev) == uint32_t(ppieces - 1)) {
+        K::finish(a, pseg, ppieces, s_w);
+        if constexpr (K::QKNORM) K::write_q_stashed(a, pseg, s_q, g, n16);
+      }
+      if (fpieces > 1 && __builtin_amdgcn_readfirstlane(fprev) == uint32_t(fpieces - 1)) {
+        K::finish(a, fseg, fpieces, s_w);
+        if constexpr (K::QKNORM) K::write_q(a, fseg, qop, g, n16);
+      }
     }
   }
 
@@ -459,21 +636,24 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
         static_cast<_Float16*>(a.out)[size_t(b) * a.Hq * D + i] = (_Float16)0.0f;
 }
 
-int stream_workers() {
-  static int workers = [] {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    return cus * 4 * PKV_STREAM_WAVES_PER_EU;
-  }();
-  return workers;
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                       n > 0
+                   ? n
+                   : 256;
+  }
+  return cus[dev];
 }
 
 template <int D, int G, bool FP8, int MODE>
 hipError_t launch_stream(const DecodeArgs& a, int B, hipStream_t stream) {
-  const int workers = stream_workers();
+  const int workers = device_cus() * 4 * stream_waves_per_eu<FP8>();
   hipLaunchKernelGGL((decode_stream_kernel<D, G, FP8, MODE>), dim3(workers), dim3(kWave), 0, stream,
                      a, B, workers);
   return hipGetLastError();

@@ -27,12 +27,22 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // so its wait for that tile's data) above the next tile's loads.
 __device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// s_waitcnt operand that waits until at most n vector memory operations of
+// the wave are outstanding (they complete in issue order) and leaves the
+// other counters alone.
+constexpr int vmcnt_at_most(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 // Read of a wave-uniform address that nothing writes during the launch (block
 // tables, context lengths) through the scalar cache.  A vector load here would
 // share the vmcnt counter with the KV loads in flight, and waiting for its
 // result would drain them too.
 __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+__device__ __forceinline__ float load_uniform_f32(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)p;
 }
 
 // Partition statistics handed from one workgroup to another inside a launch
@@ -88,6 +98,25 @@ __device__ __forceinline__ void rope_table(float* s_cos, float* s_sin, int pos, 
     const double ang = double(pos) * pow(double(theta), -2.0 * double(i) / double(D));
     double sn, cs;
     sincos(ang, &sn, &cs);
+    s_cos[i] = float(cs);
+    s_sin[i] = float(sn);
+  }
+}
+
+// Rotation frequencies f_i = theta^(-2i/D), i < D/2, in fp64, written by the
+// lanes of one wave.  They do not depend on the position, so a wave that
+// visits several sequences computes them once.
+template <int D>
+__device__ __forceinline__ void rope_freqs(double* s_f, float theta) {
+  for (int i = threadIdx.x; i < D / 2; i += kWave) s_f[i] = pow(double(theta), -2.0 * double(i) / double(D));
+}
+
+// cos / sin of pos * f_i (angle in fp64, rounded to fp32 once).
+template <int D>
+__device__ __forceinline__ void rope_angles(const double* s_f, float* s_cos, float* s_sin, int pos) {
+  for (int i = threadIdx.x; i < D / 2; i += kWave) {
+    double sn, cs;
+    sincos(double(pos) * s_f[i], &sn, &cs);
     s_cos[i] = float(cs);
     s_sin[i] = float(sn);
   }
@@ -161,8 +190,8 @@ __device__ __forceinline__ void load_mtile_at(MTile<D, FP8>& t, const DecodeArgs
   if constexpr (FP8) {
     if (rows > 0) {
       const size_t s = base / Geo::kTile;  // == block id * Hkv + kv head
-      t.ks = a.k_scale[s];
-      t.vs = a.v_scale[s];
+      t.ks = load_uniform_f32(a.k_scale + s);
+      t.vs = load_uniform_f32(a.v_scale + s);
     }
   }
 }
