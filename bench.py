@@ -37,6 +37,26 @@ from paged_kv_cache_208_amd.roofline import HBM_GBPS  # noqa: E402
 METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + decode steps/s at B"
 ROTATE_BYTES = 1 << 30
 
+# HBM bytes per launch of the one-launch step kernel (balanced split), from two
+# rocprofv3 passes (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by
+# what the counter reads for a plain 256 MiB copy (x2.0 and x1.0).  Keyed by
+# workload and a hash of the step kernel's sources: a changed kernel reports
+# traffic null until it is measured again.
+STEP_SOURCES = ("decode_stream.hip", "decode_tile.h", "device.h", "kernels.h", "shape_limits.h")
+MEASURED_TRAFFIC = {
+    ("c2", "6c86bdb0d36182e5"): {"fetch_bytes": 317310157, "write_bytes": 3321344,
+                                 "source": "profiles/step_balanced_c2_hbm_bytes.md"},
+}
+
+
+def step_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in STEP_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_208_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
@@ -250,6 +270,11 @@ def main():
 
     kv = synth.kv_bytes(cfg, d["context_lens"])
     tokens = int(d["context_lens"].astype(np.int64).sum())
+    traffic = None
+    fused_balanced = not args.unfused and step_ps == 0 and args.splits == 16
+    measured = MEASURED_TRAFFIC.get((cfg.name, step_source_hash())) if fused_balanced else None
+    if measured:
+        traffic = measured["fetch_bytes"] + measured["write_bytes"]
     value = kv / (ms * 1e-3) / 1e9
     achieved = kv / (dec_avg * 1e-3) / 1e9
     res = {
@@ -292,7 +317,9 @@ def main():
             "peak": HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "bytes per launch (HBM read + write)",
+            "traffic_detail": measured,
             "kernel": "paged_attn_decode" if args.unfused else "paged_decode_step",
             "algorithmic_bytes_per_launch": kv,
         },
