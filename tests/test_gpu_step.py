@@ -176,3 +176,87 @@ def test_step_full_size_sampled(name, balanced):
     print(f"{name} step sampled {seqs} max_abs={err:.3e}", flush=True)
     assert err <= tol
     assert torch.count_nonzero(ws[3]).item() == 0
+
+
+def _relen(d, lens):
+    """The batch with new context lengths: the new token moves to each
+    sequence's new last position (no slot for an empty sequence)."""
+    lens = np.asarray(lens, dtype=np.int32)
+    tab = d["block_tables"]
+    slots = np.array([int(tab[b, (n - 1) // 16]) * 16 + (n - 1) % 16 if n > 0 else -1
+                      for b, n in enumerate(lens)], dtype=np.int64)
+    return dict(d, context_lens=lens, slot_mapping=slots)
+
+
+@pytest.mark.parametrize("splits", [3, 16])
+def test_step_balanced_many_short_sequences(splits):
+    """More sequences than one wave scans at once (B > 64), segments of 1-3
+    tiles so one wave's range holds many segments, every fifth sequence
+    empty."""
+    cfg, d = batch("c2", B=100, len_lo=1, len_hi=48, mbs=3)
+    lens = d["context_lens"].copy()
+    lens[::5] = 0
+    d2 = _relen(d, lens)
+    g = to_device(d2)
+    out, ws = _step(cfg, g, 0, splits=splits)
+    kp, vp = append_ref(d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], d2["slot_mapping"])
+    assert np.array_equal(_u16(g["k_pool"].cpu().numpy()), _u16(kp))
+    assert np.array_equal(_u16(g["v_pool"].cpu().numpy()), _u16(vp))
+    ref = attn_ref(d["q"], kp, vp, d["block_tables"], lens, cfg.scale)
+    assert torch.all(out[::5] == 0)
+    assert max_abs(out, ref) <= TOL_F16
+    assert torch.count_nonzero(ws[3]).item() == 0
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 128), (16, 8, 64), (64, 8, 128), (8, 4, 64)])
+def test_step_balanced_group_sizes(Hq, Hkv, D):
+    cfg, d = batch("c2", B=9, Hq=Hq, Hkv=Hkv, D=D, len_lo=1, len_hi=900, mbs=57)
+    g = to_device(d)
+    out, ws = _step(cfg, g, 0)
+    kp, vp = append_ref(d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], d["slot_mapping"])
+    assert np.array_equal(_u16(g["k_pool"].cpu().numpy()), _u16(kp))
+    ref = attn_ref(d["q"], kp, vp, d["block_tables"], d["context_lens"], cfg.scale)
+    assert max_abs(out, ref) <= TOL_F16
+    assert torch.count_nonzero(ws[3]).item() == 0
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_step_balanced_e4m3_with_empty_sequences(D):
+    kw = dict(B=70, len_lo=1, len_hi=300, mbs=19)
+    if D == 64:
+        kw.update(D=64, Hq=16, Hkv=2)
+    cfg, d = batch("c5", **kw)
+    lens = d["context_lens"].copy()
+    lens[3::9] = 0
+    d2 = dict(d, context_lens=lens)
+    g = to_device(d2)
+    out, ws = _step(cfg, g, 0, append=False)
+    ref = attn_ref(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], lens, cfg.scale,
+                   k_scale=d["k_scale"], v_scale=d["v_scale"])
+    assert torch.all(out[3::9] == 0)
+    assert max_abs(out, ref) <= TOL_E4M3
+    assert torch.count_nonzero(ws[3]).item() == 0
+
+
+def test_step_balanced_qknorm_many_sequences():
+    """QK-norm + RoPE with B > 64, empty sequences and short segments: angle
+    tables change between neighbouring segments of one wave."""
+    cfg, d = batch("c4", B=80, len_lo=1, len_hi=200, mbs=13)
+    lens = d["context_lens"].copy()
+    lens[::7] = 0
+    d2 = _relen(d, lens)
+    g = to_device(d2)
+    out, ws = _step(cfg, g, 0, qknorm=True)
+    q2, kp, vp, _, _ = fused_append_ref(d["q"], d["k_new"], d["v_new"], d["k_pool"], d["v_pool"],
+                                        d2["slot_mapping"], lens, d["gamma_q"], d["gamma_k"],
+                                        cfg.eps, cfg.theta)
+    gq = g["q"].cpu().numpy()
+    live = lens > 0
+    ulp = np.spacing(np.maximum(np.abs(q2), np.abs(gq)).astype(np.float16)).astype(np.float64)
+    assert np.all((np.abs(gq.astype(np.float64) - q2.astype(np.float64)) <= ulp)[live])
+    assert np.array_equal(_u16(gq[~live]), _u16(d["q"][~live])), "q of empty sequences changed"
+    assert np.array_equal(_u16(g["v_pool"].cpu().numpy()), _u16(vp))
+    ref = attn_ref(q2, kp, vp, d["block_tables"], lens, cfg.scale)
+    assert torch.all(out[::7] == 0)
+    assert max_abs(out, ref) <= TOL_F16
+    assert torch.count_nonzero(ws[3]).item() == 0
