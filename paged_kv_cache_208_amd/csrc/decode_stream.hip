@@ -84,13 +84,15 @@ struct Totals {
   int max_tiles;
 };
 
-__device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B) {
+// L0: this lane's length in the first chunk of 64 sequences, read once by
+// the caller and used by both scans.
+__device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B, int L0) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t tot = 0;
   int mx = 0;
   for (int c = 0; c < B; c += kWave) {
     const int b = c + lane;
-    const int T = b < B ? (a.context_lens[b] + 15) / 16 : 0;
+    const int T = ((c == 0 ? L0 : b < B ? a.context_lens[b] : 0) + 15) / 16;
     const int64_t incl = wave_scan(int64_t(T));
     tot += readlane64(incl, kWave - 1);
     mx = max(mx, T);
@@ -101,13 +103,13 @@ __device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B) {
 }
 
 // Cursor of flattened tile t (t < total).
-__device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t) {
+__device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, int L0) {
   const int lane = threadIdx.x & (kWave - 1);
   Cursor c{};
   int64_t carry = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
-    const int L = b < B ? a.context_lens[b] : 0;
+    const int L = c0 == 0 ? L0 : b < B ? a.context_lens[b] : 0;
     const int64_t w = int64_t(a.Hkv) * ((L + 15) / 16);
     const int64_t hi = carry + wave_scan(w);
     const int64_t lo = hi - w;
@@ -372,13 +374,43 @@ struct StreamKernel {
   static __device__ __forceinline__ void combine(const DecodeArgs& a, size_t row0, int pieces,
                                                  float* s_w) {
     const int lane = threadIdx.x & (kWave - 1);
-    for (int t = lane; t < G * pieces; t += kWave) {
-      const int j = t / pieces, p = t % pieces;
-      const size_t pr = (row0 + j) * a.max_partitions + p;
-      s_w[2 * (j * kMaxStepPartitions + p)] = load_f32_coherent(a.part_max + pr);
-      s_w[2 * (j * kMaxStepPartitions + p) + 1] = load_f32_coherent(a.part_sum + pr);
+    constexpr int kBatch = kOwn >= 16 ? 1 : 16 / kOwn;
+    const __amdgpu_buffer_rsrc_t rs = partial_rows(a, row0);
+    // all loads of the statistics and of the first batch of partial rows go
+    // out together: one round trip when pieces <= kBatch
+    constexpr int kStat = (G * kMaxStepPartitions + kWave - 1) / kWave;
+    float mv[kStat], lv[kStat];
+#pragma unroll
+    for (int i = 0; i < kStat; ++i) {
+      const int t = lane + i * kWave;
+      mv[i] = lv[i] = 0.0f;
+      if (t < G * pieces) {
+        const size_t pr = (row0 + t / pieces) * a.max_partitions + t % pieces;
+        mv[i] = load_f32_coherent(a.part_max + pr);
+        lv[i] = load_f32_coherent(a.part_sum + pr);
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    u32x4 v[kBatch][kOwn];
+    auto load_batch = [&](int p0) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q)
+#pragma unroll
+        for (int k = 0; k < kOwn; ++k) {
+          const int c = lane + k * kWave;
+          v[q][k] = p0 + q < pieces && c < kF4 ? load16_coherent(rs, partial_offset(a, c, p0 + q))
+                                               : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    load_batch(0);
+#pragma unroll
+    for (int i = 0; i < kStat; ++i) {
+      const int t = lane + i * kWave;
+      if (t < G * pieces) {
+        const int j = t / pieces, p = t % pieces;
+        s_w[2 * (j * kMaxStepPartitions + p)] = mv[i];
+        s_w[2 * (j * kMaxStepPartitions + p) + 1] = lv[i];
+      }
+    }
     for (int j = lane; j < G; j += kWave) {
       float* w = s_w + 2 * j * kMaxStepPartitions;
       float M = -FLT_MAX;
@@ -391,22 +423,11 @@ struct StreamKernel {
       }
       w[0] = den;
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    constexpr int kBatch = kOwn >= 16 ? 1 : 16 / kOwn;
-    const __amdgpu_buffer_rsrc_t rs = partial_rows(a, row0);
     float4_t num[kOwn];
 #pragma unroll
     for (int k = 0; k < kOwn; ++k) num[k] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     for (int p0 = 0; p0 < pieces; p0 += kBatch) {
-      u32x4 v[kBatch][kOwn];
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q)
-#pragma unroll
-        for (int k = 0; k < kOwn; ++k) {
-          const int c = lane + k * kWave;
-          v[q][k] = p0 + q < pieces && c < kF4 ? load16_coherent(rs, partial_offset(a, c, p0 + q))
-                                               : u32x4{0u, 0u, 0u, 0u};
-        }
+      if (p0 > 0) load_batch(p0);
 #pragma unroll
       for (int q = 0; q < kBatch; ++q)
 #pragma unroll
@@ -458,7 +479,8 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   __shared__ float s_gq[K::QKNORM ? D : 1];          // RMSNorm weights of q and k
   __shared__ float s_gk[K::QKNORM ? D : 1];
 
-  const Totals tot = total_tiles(a, B);
+  const int L0 = lane < B ? a.context_lens[lane] : 0;
+  const Totals tot = total_tiles(a, B, L0);
   const int64_t W = tot.tiles;
   // equal shares, but long enough that no sequence's segment is cut into more
   // than max_partitions pieces: T tiles span at most (T-1)/tpw + 2 ranges
@@ -468,7 +490,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   const int64_t t1 = min(W, t0 + tpw);
 
   if (t0 < t1) {
-    Cursor cur = locate(a, B, t0);
+    Cursor cur = locate(a, B, t0, L0);
     int rope_b[2] = {-1, -1};  // sequence whose angles are in each table
     int ord = 0;                // segments entered so far; parity picks the table
     if constexpr (K::QKNORM) {
