@@ -73,6 +73,11 @@ def parse():
                    help="time append, decode and reduce as three launches")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget for the oracle baseline")
+    p.add_argument("--op", default="step", choices=("step", "copy-blocks"),
+                   help="step: the decode step (default); copy-blocks: the copy-on-write "
+                        "block copy on the config's pools")
+    p.add_argument("--copy-pairs", type=int, default=2048,
+                   help="block pairs per copy-blocks launch")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after timing, run plain device copies of this many MiB (a known-size "
                         "kernel that profiler byte counters can be scaled against)")
@@ -142,6 +147,87 @@ def _cpu_model():
 
 
 # --------------------------------------------------------------------------- GPU run
+def bench_copy_blocks(args, cfg, d):
+    """Copy-on-write block copy: `--copy-pairs` whole blocks (K and V pools,
+    all kv heads) per launch, two disjoint pair sets alternating."""
+    import torch
+
+    from paged_kv_cache_208_amd import _lib
+
+    nb = d["nb"]
+    n = min(args.copy_pairs, nb // 4)
+    rng = np.random.default_rng(208_100)
+    perm = rng.permutation(nb)
+    sets = [(perm[0:n], perm[n:2 * n]), (perm[2 * n:3 * n], perm[3 * n:4 * n])]
+    fp8 = cfg.kv_dtype == "e4m3"
+    block_bytes = cfg.Hkv * 16 * cfg.D * (1 if fp8 else 2)
+    moved = 2 * 2 * n * block_bytes + (2 * 2 * n * cfg.Hkv * 4 if fp8 else 0)  # read + write
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import copy_blocks_ref
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            copy_blocks_ref(d["k_pool"], d["v_pool"], sets[reps % 2][0], sets[reps % 2][1],
+                            d.get("k_scale"), d.get("v_scale"))
+            reps += 1
+            if time.perf_counter() - t0 > min(args.cpu_seconds, 5.0):
+                break
+        sec = (time.perf_counter() - t0) / reps
+        cpu = {"value": moved / sec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} full oracle calls ({n} pairs each, whole-pool copy-out "
+                         "included), one core"}
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+    kp, vp = up(d["k_pool"]), up(d["v_pool"])
+    ks = up(d["k_scale"]) if fp8 else None
+    vs = up(d["v_scale"]) if fp8 else None
+    pairs = [(up(a.astype(np.int32)), up(b.astype(np.int32))) for a, b in sets]
+
+    def launch(i):
+        src, dst = pairs[i % 2]
+        _lib.paged_kv_copy_blocks(kp, vp, src, dst, k_scale=ks, v_scale=vs, stream=stream)
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(K):
+        launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = moved / (ms * 1e-3) / 1e9
+    achieved = moved / (k_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "copy-on-write block copy GB/s (HBM read + write)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8" if fp8 else "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{n} block copies per launch on the pools of: {cfg.description}",
+                   "name": cfg.name, "pairs": n, "block_bytes_per_pool": block_bytes},
+        "kernel_us": round(k_ms * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_GBPS, 4), "traffic": None,
+                     "kernel": "paged_kv_copy_blocks", "algorithmic_bytes_per_launch": moved},
+        "cpu_baseline": cpu,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -158,6 +244,10 @@ def main():
     print(f"# generated {cfg.name} in {time.perf_counter() - t0:.1f}s: B={cfg.B} "
           f"Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} kv={cfg.kv_dtype} PS={cfg.partition_size} "
           f"NB={d['nb']}", file=sys.stderr, flush=True)
+
+    if args.op == "copy-blocks":
+        bench_copy_blocks(args, cfg, d)
+        return
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -178,6 +178,30 @@ int paged_decode_step(void* out, void* q, const void* k_new, const void* v_new, 
                       float rope_theta, float* part_out, float* part_max, float* part_sum,
                       uint32_t* counters, int max_partitions, void* stream);
 
+/*
+ * paged_kv_copy_blocks - copy whole physical blocks for copy-on-write.
+ *
+ * "Distributed LLM Inference Serving Platform", section 11 (worked solution
+ * of Lab 1, copy-on-write for parallel sampling) and section 7 (block
+ * manager): a sequence that appends into a tail block other sequences still
+ * share takes a fresh block and the tokens already written are copied into
+ * it.  For every i < n:
+ *     k_pool[dst[i]] = k_pool[src[i]],  v_pool[dst[i]] = v_pool[src[i]]
+ * (all Hkv heads and BS rows of the block), and with kv_dtype PKV_KV_E4M3
+ *     k_scale[dst[i]][:] = k_scale[src[i]][:],  v_scale likewise.
+ * Nothing else changes.
+ *
+ * k_pool, v_pool [NB][Hkv][BS][D] fp16 or E4M3 bytes (device, 16-byte
+ * aligned); k_scale, v_scale [NB][Hkv] fp32 (device, E4M3 only, else
+ * ignored); src, dst [n] int32 (device).  n == 0 is a no-op.
+ * Device-data contract (not checked): 0 <= src[i], dst[i] < NB; the dst[i]
+ * are distinct and none of them is also a source (otherwise the result is
+ * undefined).  One workgroup per (pair, pool); the copy is HBM bound.
+ */
+int paged_kv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                         const int32_t* src, const int32_t* dst, int n, int Hkv, int D, int BS,
+                         int64_t NB, int kv_dtype, void* stream);
+
 /* Bytes of part_out + part_max + part_sum for the given sizes (0 on overflow). */
 size_t paged_attn_workspace_size(int B, int Hq, int D, int max_partitions);
 
@@ -210,6 +234,9 @@ int pkv_validate_step(const void* out, const void* q, const void* k_new, const v
 int pkv_validate_reduce(const void* out, const float* part_out, const float* part_max,
                         const float* part_sum, const int32_t* context_lens, int B, int Hq,
                         int D, int partition_size, int max_partitions);
+int pkv_validate_copy(const void* k_pool, const void* v_pool, const float* k_scale,
+                      const float* v_scale, const int32_t* src, const int32_t* dst, int n,
+                      int Hkv, int D, int BS, int64_t NB, int kv_dtype);
 
 #ifdef __cplusplus
 }

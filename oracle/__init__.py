@@ -19,6 +19,8 @@ Sources followed (page title, section):
   * Same page, section 5.1 (request lifecycle): each decode step writes the
     new token's K/V into its physical block, then attends over every block in
     the sequence's table.
+  * Same page, section 11 (Lab 1 worked solution) and section 7 (block
+    manager): copy-on-write clones a shared tail block into a fresh one.
   * "Roadmap: vLLM-style serving features for TornadoVM batched decode",
     Core batched decode (per-head QK-norm + split-half RoPE for Qwen3),
     Serving / scheduling (PagedAttention: block-pool KV + per-slot block
@@ -38,3 +40,4 @@ from .attention import (  # noqa: F401
 )
 from .e4m3 import e4m3_table, e4m3_decode  # noqa: F401
 from .append import append_ref, rmsnorm_rope_ref, fused_append_ref  # noqa: F401
+from .blocks import copy_blocks_ref  # noqa: F401

@@ -37,6 +37,7 @@ _SIGNATURES = {
     "paged_attn_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                _I64, _F, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I, _P]),
+    "paged_kv_copy_blocks": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I, _P]),
     "paged_attn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "pkv_strerror": (ctypes.c_char_p, [_I]),
     "pkv_validate_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
@@ -44,6 +45,7 @@ _SIGNATURES = {
     "pkv_validate_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64,
                                  _F, _I, _I, _P, _P, _P, _I]),
     "pkv_validate_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I]),
+    "pkv_validate_copy": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I]),
     "pkv_validate_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                _I64, _F, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I]),
 }
@@ -142,6 +144,28 @@ def paged_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, *, q=None, gamma
                                _ptr(gamma_q), _ptr(gamma_k), _ptr(context_lens), float(eps),
                                float(rope_theta), _stream(stream))
     _raise("paged_kv_append", st)
+
+
+def paged_kv_copy_blocks(k_pool, v_pool, src, dst, *, k_scale=None, v_scale=None, stream=None):
+    """Copy whole physical blocks src[i] -> dst[i] in both pools (and their
+    E4M3 scales): the data side of copy-on-write."""
+    if k_pool.dtype not in (torch.float16, torch.uint8) or v_pool.dtype != k_pool.dtype:
+        raise TypeError("pools must both be float16 or both uint8 (E4M3)")
+    _check(k_pool, "k_pool", k_pool.dtype, 4)
+    _check(v_pool, "v_pool", k_pool.dtype, 4)
+    _check(src, "src", torch.int32, 1)
+    _check(dst, "dst", torch.int32, 1)
+    if v_pool.shape != k_pool.shape or src.shape != dst.shape:
+        raise ValueError("pool shapes or src/dst lengths disagree")
+    NB, Hkv, BS, D = k_pool.shape
+    kv = _kv_dtype(k_pool)
+    if kv == PKV_KV_E4M3:
+        _check(k_scale, "k_scale", torch.float32, 2)
+        _check(v_scale, "v_scale", torch.float32, 2)
+    st = lib().paged_kv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(src), _ptr(dst), src.shape[0], Hkv, D, BS, NB, kv,
+                                    _stream(stream))
+    _raise("paged_kv_copy_blocks", st)
 
 
 def max_partitions_for(max_blocks_per_seq: int, partition_size: int) -> int:

@@ -135,3 +135,16 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
   return launch_status(pkv::launch_decode_step(a, B, D, Hq / Hkv, fp8, mode,
                                                static_cast<hipStream_t>(stream)));
 }
+
+extern "C" int paged_kv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                    const int32_t* src, const int32_t* dst, int n, int Hkv,
+                                    int D, int BS, int64_t NB, int kv_dtype, void* stream) {
+  const int st =
+      pkv_validate_copy(k_pool, v_pool, k_scale, v_scale, src, dst, n, Hkv, D, BS, NB, kv_dtype);
+  if (st != PKV_OK || n == 0) return st;
+  const bool fp8 = kv_dtype == PKV_KV_E4M3;
+  pkv::CopyArgs a{static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                  fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr, src, dst,
+                  int64_t(Hkv) * BS * D * (fp8 ? 1 : 2), Hkv};
+  return launch_status(pkv::launch_copy_blocks(a, n, static_cast<hipStream_t>(stream)));
+}

@@ -62,6 +62,17 @@ struct AppendArgs {
   float eps, theta;
 };
 
+struct CopyArgs {
+  uint8_t* k_pool;            // [NB][Hkv][16][D] elements of elem_bytes
+  uint8_t* v_pool;
+  float* k_scale;             // [NB][Hkv], E4M3 only (else null)
+  float* v_scale;
+  const int32_t* src;         // [n]
+  const int32_t* dst;
+  int64_t block_bytes;        // Hkv * 16 * D * elem_bytes (a multiple of 16)
+  int Hkv;
+};
+
 // Tile engine of the decode kernel (same result, different instruction mix).
 enum class DecodeEngine { kMfma, kValu };
 
@@ -74,5 +85,6 @@ hipError_t launch_decode_stream(const DecodeArgs& a, int B, int D, int group, bo
                                 hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int B, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int T, int D, bool fused, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t stream);
 
 }  // namespace pkv

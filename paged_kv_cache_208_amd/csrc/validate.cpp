@@ -169,3 +169,22 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
   }
   return PKV_OK;
 }
+
+extern "C" int pkv_validate_copy(const void* k_pool, const void* v_pool, const float* k_scale,
+                                 const float* v_scale, const int32_t* src, const int32_t* dst,
+                                 int n, int Hkv, int D, int BS, int64_t NB, int kv_dtype) {
+  if (n < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB <= 0) return PKV_EINVAL;
+  if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_E4M3) return PKV_EINVAL;
+  if (!supported_head_dim(D)) return PKV_EUNSUPPORTED;
+  if (BS != pkv::kBlockSize) return PKV_EUNSUPPORTED;
+  if (int64_t(n) > pkv::kMaxGrid) return PKV_EUNSUPPORTED;
+  if (n == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src || !dst) return PKV_EINVAL;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(src, 4) || !aligned(dst, 4))
+    return PKV_EINVAL;
+  if (kv_dtype == PKV_KV_E4M3) {
+    if (!k_scale || !v_scale) return PKV_EINVAL;
+    if (!aligned(k_scale, 4) || !aligned(v_scale, 4)) return PKV_EINVAL;
+  }
+  return PKV_OK;
+}

@@ -208,3 +208,26 @@ def test_step_validation_codes(lib, kw, code):
     assert lib.pkv_validate_step(*_step_args(**kw).values()) == code
     if code != 0:
         assert lib.paged_decode_step(*_step_args(**kw).values(), None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    (dict(n=0, src=None, dst=None), 0),
+    (dict(n=-1), -1),
+    (dict(src=None), -1),
+    (dict(k_pool=MIS), -1),
+    (dict(dst=A + 2), -1),
+    (dict(D=96), -2),
+    (dict(BS=32), -2),
+    (dict(kv_dtype=2), -1),
+    (dict(kv_dtype=1), -1),
+    (dict(kv_dtype=1, k_scale=A, v_scale=A), 0),
+    (dict(NB=0), -1),
+])
+def test_copy_validation_codes(lib, kw, code):
+    a = dict(k_pool=A, v_pool=A, k_scale=None, v_scale=None, src=A, dst=A, n=3, Hkv=8, D=128,
+             BS=16, NB=100, kv_dtype=0)
+    a.update(kw)
+    assert lib.pkv_validate_copy(*a.values()) == code
+    if code != 0:
+        assert lib.paged_kv_copy_blocks(*a.values(), None) == code
