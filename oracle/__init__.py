@@ -41,3 +41,5 @@ from .attention import (  # noqa: F401
 from .e4m3 import e4m3_table, e4m3_decode  # noqa: F401
 from .append import append_ref, rmsnorm_rope_ref, fused_append_ref  # noqa: F401
 from .blocks import copy_blocks_ref  # noqa: F401
+from .e4m3 import e4m3_encode  # noqa: F401
+from .fp8_append import append_e4m3_ref  # noqa: F401
