@@ -73,9 +73,10 @@ def parse():
                    help="time append, decode and reduce as three launches")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget for the oracle baseline")
-    p.add_argument("--op", default="step", choices=("step", "copy-blocks"),
+    p.add_argument("--op", default="step", choices=("step", "copy-blocks", "append-e4m3"),
                    help="step: the decode step (default); copy-blocks: the copy-on-write "
-                        "block copy on the config's pools")
+                        "block copy on the config's pools; append-e4m3: appending one token "
+                        "per sequence into E4M3 blocks (use an E4M3 config, c5)")
     p.add_argument("--copy-pairs", type=int, default=2048,
                    help="block pairs per copy-blocks launch")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -228,6 +229,64 @@ def bench_copy_blocks(args, cfg, d):
     }), flush=True)
 
 
+def bench_append_e4m3(args, cfg, d):
+    """One token per sequence appended into E4M3 blocks at each sequence's
+    next position (sequences whose last block is full skip the step)."""
+    import torch
+
+    from paged_kv_cache_208_amd import _lib
+
+    if cfg.kv_dtype != "e4m3":
+        raise SystemExit("--op append-e4m3 needs an E4M3 config (c5)")
+    rng = np.random.default_rng(208_200)
+    B, Hkv, D = cfg.B, cfg.Hkv, cfg.D
+    lens = d["context_lens"].astype(np.int64)
+    tab = d["block_tables"]
+    slots = np.array([int(tab[b, L // 16]) * 16 + L % 16 if L % 16 else -1
+                      for b, L in enumerate(lens)], dtype=np.int64)
+    kn = rng.standard_normal((B, Hkv, D)).astype(np.float16)
+    vn = rng.standard_normal((B, Hkv, D)).astype(np.float16)
+    live = int((slots >= 0).sum())
+    # algorithmic bytes when no row is re-encoded: new rows in (fp16), codes out, scales
+    moved = live * Hkv * 2 * (D * 2 + D + 8)
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+    g = {k: up(v) for k, v in (("kp", d["k_pool"]), ("vp", d["v_pool"]), ("ks", d["k_scale"]),
+                               ("vs", d["v_scale"]), ("kn", kn), ("vn", vn), ("sl", slots))}
+
+    def launch():
+        _lib.paged_kv_append_e4m3(g["kn"], g["vn"], g["kp"], g["vp"], g["ks"], g["vs"], g["sl"],
+                                  stream=stream)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    K = args.steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(K):
+        launch()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    print(json.dumps({
+        "metric": "E4M3 append latency per step (us) and GB/s",
+        "value": round(ms * 1e3, 3), "unit": "us", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"one token per sequence ({live} of {B}) into the E4M3 pools of: "
+                               f"{cfg.description}", "name": cfg.name},
+        "gbps": round(moved / (ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "latency", "achieved": round(moved / (ms * 1e-3) / 1e9, 2),
+                     "peak": HBM_GBPS, "unit": "GB/s",
+                     "frac": round(moved / (ms * 1e-3) / 1e9 / HBM_GBPS, 5), "traffic": None,
+                     "kernel": "paged_kv_append_e4m3", "algorithmic_bytes_per_launch": moved},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -247,6 +306,9 @@ def main():
 
     if args.op == "copy-blocks":
         bench_copy_blocks(args, cfg, d)
+        return
+    if args.op == "append-e4m3":
+        bench_append_e4m3(args, cfg, d)
         return
 
     cpu = None

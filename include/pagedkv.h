@@ -179,6 +179,34 @@ int paged_decode_step(void* out, void* q, const void* k_new, const void* v_new, 
                       uint32_t* counters, int max_partitions, void* stream);
 
 /*
+ * paged_kv_append_e4m3 - write this step's new K/V rows into E4M3 blocks,
+ * keeping each (block, kv head) scale valid.
+ *
+ * The quantized (Q8/FP8) KV cache is a listed item of "Roadmap: vLLM-style
+ * serving features for TornadoVM batched decode" (Sampling / logits); the
+ * pages fix no policy.  The one implemented keeps a block's scale at the
+ * running amax of its rows divided by 448 (the largest E4M3 value).  For
+ * token i with p = slot_mapping[i] >= 0, block n = p / BS, row r = p % BS,
+ * and for K and V of every kv head h separately, in float32:
+ *     a = max_d |new[i][h][d]|;  s_old = r > 0 ? scale[n][h] : 0
+ *     if a > 448 * s_old: s_new = a / 448, and rows 0..r-1 of the block are
+ *         re-encoded c' = enc((dec(c) * s_old) / s_new)  (skipped if s_old = 0)
+ *     else s_new = s_old
+ *     row r = enc(new / s_new) (zeros while s_new = 0);  scale[n][h] = s_new
+ * enc rounds to the nearest E4M3 value (ties to even) after clamping to
+ * +-448; dec is exact.  Rows past r and every other block are untouched.
+ *
+ * k_new, v_new [T][Hkv][D] fp16; k_pool, v_pool [NB][Hkv][BS][D] E4M3 codes
+ * (uint8); k_scale, v_scale [NB][Hkv] fp32; slot_mapping [T] int64; all
+ * device memory, pools and rows 16-byte aligned.  T == 0 is a no-op.
+ * Device-data contract (not checked): the slots of one call lie in distinct
+ * blocks (one wave owns a block's scale while it updates it).
+ */
+int paged_kv_append_e4m3(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                         float* k_scale, float* v_scale, const int64_t* slot_mapping, int T,
+                         int Hkv, int D, int BS, int64_t NB, void* stream);
+
+/*
  * paged_kv_copy_blocks - copy whole physical blocks for copy-on-write.
  *
  * "Distributed LLM Inference Serving Platform", section 11 (worked solution
@@ -234,6 +262,10 @@ int pkv_validate_step(const void* out, const void* q, const void* k_new, const v
 int pkv_validate_reduce(const void* out, const float* part_out, const float* part_max,
                         const float* part_sum, const int32_t* context_lens, int B, int Hq,
                         int D, int partition_size, int max_partitions);
+int pkv_validate_append_e4m3(const void* k_new, const void* v_new, const void* k_pool,
+                             const void* v_pool, const float* k_scale, const float* v_scale,
+                             const int64_t* slot_mapping, int T, int Hkv, int D, int BS,
+                             int64_t NB);
 int pkv_validate_copy(const void* k_pool, const void* v_pool, const float* k_scale,
                       const float* v_scale, const int32_t* src, const int32_t* dst, int n,
                       int Hkv, int D, int BS, int64_t NB, int kv_dtype);

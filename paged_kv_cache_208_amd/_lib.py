@@ -38,6 +38,7 @@ _SIGNATURES = {
     "paged_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                _I64, _F, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I, _P]),
     "paged_kv_copy_blocks": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I, _P]),
+    "paged_kv_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P]),
     "paged_attn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "pkv_strerror": (ctypes.c_char_p, [_I]),
     "pkv_validate_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
@@ -46,6 +47,7 @@ _SIGNATURES = {
                                  _F, _I, _I, _P, _P, _P, _I]),
     "pkv_validate_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I]),
     "pkv_validate_copy": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I]),
+    "pkv_validate_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64]),
     "pkv_validate_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                _I64, _F, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I]),
 }
@@ -144,6 +146,29 @@ def paged_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, *, q=None, gamma
                                _ptr(gamma_q), _ptr(gamma_k), _ptr(context_lens), float(eps),
                                float(rope_theta), _stream(stream))
     _raise("paged_kv_append", st)
+
+
+def paged_kv_append_e4m3(k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, *,
+                         stream=None):
+    """Quantise new K/V rows into E4M3 blocks, keeping each (block, kv head)
+    scale at the running amax / 448 (earlier rows re-encoded when it grows)."""
+    _check(k_new, "k_new", torch.float16, 3)
+    _check(v_new, "v_new", torch.float16, 3)
+    _check(k_pool, "k_pool", torch.uint8, 4)
+    _check(v_pool, "v_pool", torch.uint8, 4)
+    _check(k_scale, "k_scale", torch.float32, 2)
+    _check(v_scale, "v_scale", torch.float32, 2)
+    _check(slot_mapping, "slot_mapping", torch.int64, 1)
+    T, Hkv, D = k_new.shape
+    NB, hkv2, BS, d2 = k_pool.shape
+    if v_new.shape != k_new.shape or slot_mapping.shape[0] != T or (hkv2, d2) != (Hkv, D) \
+            or v_pool.shape != k_pool.shape or tuple(k_scale.shape) != (NB, Hkv) \
+            or v_scale.shape != k_scale.shape:
+        raise ValueError("shapes of rows, pools, scales and slots disagree")
+    st = lib().paged_kv_append_e4m3(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                    _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping), T, Hkv,
+                                    D, BS, NB, _stream(stream))
+    _raise("paged_kv_append_e4m3", st)
 
 
 def paged_kv_copy_blocks(k_pool, v_pool, src, dst, *, k_scale=None, v_scale=None, stream=None):

@@ -148,3 +148,15 @@ extern "C" int paged_kv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, 
                   int64_t(Hkv) * BS * D * (fp8 ? 1 : 2), Hkv};
   return launch_status(pkv::launch_copy_blocks(a, n, static_cast<hipStream_t>(stream)));
 }
+
+extern "C" int paged_kv_append_e4m3(const void* k_new, const void* v_new, void* k_pool,
+                                    void* v_pool, float* k_scale, float* v_scale,
+                                    const int64_t* slot_mapping, int T, int Hkv, int D, int BS,
+                                    int64_t NB, void* stream) {
+  const int st = pkv_validate_append_e4m3(k_new, v_new, k_pool, v_pool, k_scale, v_scale,
+                                          slot_mapping, T, Hkv, D, BS, NB);
+  if (st != PKV_OK || T == 0) return st;
+  pkv::AppendE4m3Args a{k_new, v_new, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                        k_scale, v_scale, slot_mapping, Hkv};
+  return launch_status(pkv::launch_append_e4m3(a, T, D, static_cast<hipStream_t>(stream)));
+}

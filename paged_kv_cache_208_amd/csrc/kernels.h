@@ -62,6 +62,17 @@ struct AppendArgs {
   float eps, theta;
 };
 
+struct AppendE4m3Args {
+  const void* k_new;          // [T][Hkv][D] fp16
+  const void* v_new;
+  uint8_t* k_pool;            // [NB][Hkv][16][D] E4M3 codes
+  uint8_t* v_pool;
+  float* k_scale;             // [NB][Hkv]
+  float* v_scale;
+  const int64_t* slot_mapping;  // [T]
+  int Hkv;
+};
+
 struct CopyArgs {
   uint8_t* k_pool;            // [NB][Hkv][16][D] elements of elem_bytes
   uint8_t* v_pool;
@@ -86,5 +97,6 @@ hipError_t launch_decode_stream(const DecodeArgs& a, int B, int D, int group, bo
 hipError_t launch_reduce(const ReduceArgs& a, int B, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int T, int D, bool fused, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t stream);
+hipError_t launch_append_e4m3(const AppendE4m3Args& a, int T, int D, hipStream_t stream);
 
 }  // namespace pkv

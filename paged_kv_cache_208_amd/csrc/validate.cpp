@@ -188,3 +188,21 @@ extern "C" int pkv_validate_copy(const void* k_pool, const void* v_pool, const f
   }
   return PKV_OK;
 }
+
+extern "C" int pkv_validate_append_e4m3(const void* k_new, const void* v_new, const void* k_pool,
+                                        const void* v_pool, const float* k_scale,
+                                        const float* v_scale, const int64_t* slot_mapping, int T,
+                                        int Hkv, int D, int BS, int64_t NB) {
+  if (T < 0 || Hkv <= 0 || NB <= 0 || D <= 0 || BS <= 0) return PKV_EINVAL;
+  if (!supported_head_dim(D)) return PKV_EUNSUPPORTED;
+  if (BS != pkv::kBlockSize) return PKV_EUNSUPPORTED;
+  if (int64_t(T) > pkv::kMaxGrid || Hkv > 65535) return PKV_EUNSUPPORTED;
+  if (T == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale || !slot_mapping)
+    return PKV_EINVAL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) ||
+      !aligned(v_pool, 16) || !aligned(k_scale, 4) || !aligned(v_scale, 4) ||
+      !aligned(slot_mapping, 8))
+    return PKV_EINVAL;
+  return PKV_OK;
+}

@@ -231,3 +231,23 @@ def test_copy_validation_codes(lib, kw, code):
     assert lib.pkv_validate_copy(*a.values()) == code
     if code != 0:
         assert lib.paged_kv_copy_blocks(*a.values(), None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    (dict(T=0, k_new=None), 0),
+    (dict(T=-1), -1),
+    (dict(k_scale=None), -1),
+    (dict(v_scale=A + 2), -1),
+    (dict(slot_mapping=A + 4), -1),
+    (dict(D=32), -2),
+    (dict(BS=32), -2),
+    (dict(NB=0), -1),
+])
+def test_append_e4m3_validation_codes(lib, kw, code):
+    a = dict(k_new=A, v_new=A, k_pool=A, v_pool=A, k_scale=A, v_scale=A, slot_mapping=A, T=4,
+             Hkv=8, D=128, BS=16, NB=100)
+    a.update(kw)
+    assert lib.pkv_validate_append_e4m3(*a.values()) == code
+    if code != 0:
+        assert lib.paged_kv_append_e4m3(*a.values(), None) == code
