@@ -92,12 +92,19 @@ def attn_weights_ref(q, k_pool, block_tables, context_lens, scale, *,
 
 
 def attn_ref(q, k_pool, v_pool, block_tables, context_lens, scale, *,
-             k_scale=None, v_scale=None, block_size=16, seqs=None):
+             k_scale=None, v_scale=None, block_size=16, seqs=None, window=0):
     """float64 [B, Hq, D] attention output (unrounded).
 
     L_b = 0 gives a zero row (no tokens to attend over; this library's
     convention, the pages never reach that case).  ``seqs`` restricts the
     work to the listed sequences; other rows are left NaN.
+
+    window > 0: sliding-window attention ("Roadmap: vLLM-style serving
+    features for TornadoVM batched decode", Models: the Gemma 4 batched
+    decode has sliding-window layers; the pages give no detail).  Reading
+    taken: the query at position L_b - 1 attends to the last ``window``
+    tokens, positions max(0, L_b - window) .. L_b - 1; window = 0 is full
+    attention.
     """
     B, Hq, D = q.shape
     Hkv = k_pool.shape[1]
@@ -112,6 +119,8 @@ def attn_ref(q, k_pool, v_pool, block_tables, context_lens, scale, *,
             continue
         K = gather_sequence_kv(k_pool, k_scale, block_tables[b], L, block_size)
         V = gather_sequence_kv(v_pool, v_scale, block_tables[b], L, block_size)
+        if window > 0 and L > window:
+            K, V = K[:, L - window:], V[:, L - window:]
         for h in range(Hq):
             j = h // g
             s = float(scale) * (K[j] @ q[b, h].astype(np.float64))
