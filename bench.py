@@ -69,6 +69,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=16,
                    help="most pieces one sequence is cut into by the balanced split")
+    p.add_argument("--window", type=int, default=0,
+                   help="sliding window in tokens (balanced one-launch step only; 0 = full)")
     p.add_argument("--unfused", action="store_true",
                    help="time append, decode and reduce as three launches")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -379,7 +381,7 @@ def main():
         _lib.paged_decode_step(out, g["q"], g["k_pool"], g["v_pool"], g["block_tables"],
                                g["context_lens"], cfg.scale, k_scale=g.get("k_scale"),
                                v_scale=g.get("v_scale"), partition_size=step_ps,
-                               workspace=step_ws, stream=stream, **kw)
+                               window=args.window, workspace=step_ws, stream=stream, **kw)
         if timed:
             ev["d1"][i].record(stream)
 
@@ -420,10 +422,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    kv = synth.kv_bytes(cfg, d["context_lens"])
+    kv = synth.kv_bytes(cfg, d["context_lens"], args.window)
     tokens = int(d["context_lens"].astype(np.int64).sum())
     traffic = None
-    fused_balanced = not args.unfused and step_ps == 0 and args.splits == 16
+    fused_balanced = not args.unfused and step_ps == 0 and args.splits == 16 and not args.window
     measured = MEASURED_TRAFFIC.get((cfg.name, step_source_hash())) if fused_balanced else None
     if measured:
         traffic = measured["fetch_bytes"] + measured["write_bytes"]
@@ -454,6 +456,7 @@ def main():
                      ("qknorm_rope+append+attend+combine" if cfg.fused_append
                       else "append+attend+combine")),
             "launches_per_step": (3 if not fp8 else 2) if args.unfused and PS else 1,
+            "window": args.window,
             "rotated_copies": R,
         },
         "steps_per_s": round(1e3 / ms, 1),

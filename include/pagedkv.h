@@ -166,6 +166,12 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
  *   memory, all zero before the first call; each call leaves them zero
  *   again.  Calls sharing counters, scratch or pools must not run
  *   concurrently.
+ * window > 0: sliding window ("Roadmap: vLLM-style serving features for
+ *   TornadoVM batched decode", Models: Gemma 4's sliding-window layers):
+ *   the query attends to positions max(0, L_b - window) .. L_b - 1 only, and
+ *   blocks before the window are not read.  Balanced split only
+ *   (partition_size == 0, else PKV_EUNSUPPORTED); window == 0 is full
+ *   attention, window < 0 is PKV_EINVAL.
  * kv_dtype PKV_KV_E4M3: attend + combine only (k_new must be NULL).
  * L_b == 0: zero output row, nothing written to the pools, q untouched.
  * Errors and shape limits as for paged_attn_decode and paged_kv_append.
@@ -174,9 +180,9 @@ int paged_decode_step(void* out, void* q, const void* k_new, const void* v_new, 
                       void* v_pool, const float* k_scale, const float* v_scale,
                       const int32_t* block_tables, const int32_t* context_lens, int B, int Hq,
                       int Hkv, int D, int BS, int MBS, int64_t NB, float scale, int kv_dtype,
-                      int partition_size, const float* gamma_q, const float* gamma_k, float eps,
-                      float rope_theta, float* part_out, float* part_max, float* part_sum,
-                      uint32_t* counters, int max_partitions, void* stream);
+                      int partition_size, int window, const float* gamma_q, const float* gamma_k,
+                      float eps, float rope_theta, float* part_out, float* part_max,
+                      float* part_sum, uint32_t* counters, int max_partitions, void* stream);
 
 /*
  * paged_kv_append_e4m3 - write this step's new K/V rows into E4M3 blocks,
@@ -256,9 +262,9 @@ int pkv_validate_step(const void* out, const void* q, const void* k_new, const v
                       const float* v_scale, const int32_t* block_tables,
                       const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
                       int MBS, int64_t NB, float scale, int kv_dtype, int partition_size,
-                      const float* gamma_q, const float* gamma_k, float eps, float rope_theta,
-                      const float* part_out, const float* part_max, const float* part_sum,
-                      const uint32_t* counters, int max_partitions);
+                      int window, const float* gamma_q, const float* gamma_k, float eps,
+                      float rope_theta, const float* part_out, const float* part_max,
+                      const float* part_sum, const uint32_t* counters, int max_partitions);
 int pkv_validate_reduce(const void* out, const float* part_out, const float* part_max,
                         const float* part_sum, const int32_t* context_lens, int B, int Hq,
                         int D, int partition_size, int max_partitions);

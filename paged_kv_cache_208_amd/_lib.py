@@ -36,7 +36,7 @@ _SIGNATURES = {
                                _F, _I, _I, _P, _P, _P, _I, _P]),
     "paged_attn_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
-                               _I64, _F, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I, _P]),
+                               _I64, _F, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I, _P]),
     "paged_kv_copy_blocks": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I, _P]),
     "paged_kv_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P]),
     "paged_attn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
@@ -49,7 +49,7 @@ _SIGNATURES = {
     "pkv_validate_copy": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I]),
     "pkv_validate_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64]),
     "pkv_validate_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
-                               _I64, _F, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I]),
+                               _I64, _F, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I]),
 }
 
 
@@ -297,12 +297,14 @@ def alloc_step_workspace(B, Hq, Hkv, D, max_partitions, device="cuda"):
 
 
 def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale, *, k_new=None,
-                      v_new=None, k_scale=None, v_scale=None, partition_size=0, gamma_q=None,
-                      gamma_k=None, eps=1e-6, rope_theta=1e6, workspace=None, stream=None):
+                      v_new=None, k_scale=None, v_scale=None, partition_size=0, window=0,
+                      gamma_q=None, gamma_k=None, eps=1e-6, rope_theta=1e6, workspace=None,
+                      stream=None):
     """Append (optional, + Qwen3 QK-norm/RoPE) + decode + combine in one launch.
     ``workspace`` is alloc_step_workspace(...)'s tuple.  partition_size 0
     splits contexts evenly over all waves into at most workspace-depth
-    pieces; > 0 uses fixed partitions."""
+    pieces; > 0 uses fixed partitions.  window > 0 attends to the last
+    `window` tokens only (balanced split)."""
     _check(out, "out", torch.float16, 3)
     _check(q, "q", torch.float16, 3)
     kv = _kv_dtype(k_pool)
@@ -339,7 +341,7 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
     st = lib().paged_decode_step(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
                                  _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                                  _ptr(context_lens), B, Hq, Hkv, D, BS, block_tables.shape[1], NB,
-                                 float(scale), kv, int(partition_size), _ptr(gamma_q),
+                                 float(scale), kv, int(partition_size), int(window), _ptr(gamma_q),
                                  _ptr(gamma_k), float(eps), float(rope_theta), _ptr(po), _ptr(pm),
                                  _ptr(ps), _ptr(ctr), P, _stream(stream))
     _raise("paged_decode_step", st)

@@ -58,8 +58,16 @@ constexpr int stream_waves_per_eu() {
 struct Cursor {
   int b, kvh, n;  // sequence, kv head, tile within the segment
   int L, T;       // context length of b, tiles per segment
+  int f;          // block-table index of the segment's first tile
   int64_t S;      // flattened index of the segment's first tile
 };
+
+// With a sliding window of W tokens (W > 0) a sequence of length L reads
+// positions max(0, L - W) .. L - 1: its segment starts at the tile holding
+// the first of them.
+__device__ __forceinline__ int window_start(int L, int W) { return (W > 0 && L > W) ? L - W : 0; }
+__device__ __forceinline__ int first_tile(int L, int W) { return window_start(L, W) / 16; }
+__device__ __forceinline__ int seg_tiles(int L, int W) { return (L + 15) / 16 - first_tile(L, W); }
 
 __device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
   const int lo = __builtin_amdgcn_readlane(int(uint64_t(v) & 0xffffffffu), lane);
@@ -92,7 +100,7 @@ __device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B, int L0
   int mx = 0;
   for (int c = 0; c < B; c += kWave) {
     const int b = c + lane;
-    const int T = ((c == 0 ? L0 : b < B ? a.context_lens[b] : 0) + 15) / 16;
+    const int T = seg_tiles(c == 0 ? L0 : b < B ? a.context_lens[b] : 0, a.window);
     const int64_t incl = wave_scan(int64_t(T));
     tot += readlane64(incl, kWave - 1);
     mx = max(mx, T);
@@ -110,7 +118,7 @@ __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, 
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
     const int L = c0 == 0 ? L0 : b < B ? a.context_lens[b] : 0;
-    const int64_t w = int64_t(a.Hkv) * ((L + 15) / 16);
+    const int64_t w = int64_t(a.Hkv) * seg_tiles(L, a.window);
     const int64_t hi = carry + wave_scan(w);
     const int64_t lo = hi - w;
     const uint64_t here = __builtin_amdgcn_ballot_w64(b < B && lo <= t && t < hi);
@@ -118,7 +126,8 @@ __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, 
       const int src = __builtin_ctzll(here);
       c.b = c0 + src;
       c.L = __builtin_amdgcn_readlane(L, src);
-      c.T = (c.L + 15) / 16;
+      c.T = seg_tiles(c.L, a.window);
+      c.f = first_tile(c.L, a.window);
       const int64_t off = t - readlane64(lo, src);
       c.kvh = int(off / c.T);
       c.n = int(off % c.T);
@@ -141,12 +150,14 @@ __device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B) {
     if (++c.b >= B) return;
     c.L = load_uniform(a.context_lens + c.b);
   } while (c.L == 0);
-  c.T = (c.L + 15) / 16;
+  c.T = seg_tiles(c.L, a.window);
+  c.f = first_tile(c.L, a.window);
 }
 
 // What the loop needs to know about a tile besides its data.
 struct Meta {
-  int b, kvh, n, L, T;
+  int b, kvh, n, L, T, f;
+  int lo;      // rows of the tile before the window (first tile only)
   int id;      // physical block of the tile
   int slot;    // angle table of the segment (QK-norm modes)
   int64_t S;
@@ -158,8 +169,10 @@ __device__ __forceinline__ Meta meta_of(const Cursor& c, const DecodeArgs& a, in
                                         int64_t t1) {
   Meta m;
   // a scalar load; its result is first needed one loop step later
-  m.id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + c.n);
+  m.id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + c.f + c.n);
   m.slot = 0;
+  m.f = c.f;
+  m.lo = c.n == 0 ? window_start(c.L, a.window) - 16 * c.f : 0;
   m.b = c.b;
   m.kvh = c.kvh;
   m.n = c.n;
@@ -206,7 +219,7 @@ struct StreamKernel {
                                                      const float* s_gk) {
     using VW = typename Words<Geo::kVWords>::T;
     while (c.S + c.T - 1 < t1) {
-      const int id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + (c.T - 1));
+      const int id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + (c.f + c.T - 1));
       const size_t row = size_t(c.b) * a.Hkv + c.kvh;
       const _Float16* kn = static_cast<const _Float16*>(a.k_new) + row * D;
       const _Float16* vn = static_cast<const _Float16*>(a.v_new) + row * D;
@@ -242,7 +255,8 @@ struct StreamKernel {
   static __device__ __forceinline__ void issue(MTile<D, FP8>& t, const DecodeArgs& a, const Meta& m,
                                                bool live, int k_off, int v_off) {
     const size_t base = live ? (size_t(m.id) * a.Hkv + m.kvh) * Geo::kTile : 0;
-    load_mtile_at<D, FP8>(t, a, base, live ? min(16, m.L - 16 * m.n) : 0, k_off, v_off);
+    load_mtile_at<D, FP8>(t, a, base, live ? min(16, m.L - 16 * (m.f + m.n)) : 0, k_off, v_off);
+    t.lo = live ? m.lo : 0;
   }
 
   // Pieces the wave ranges cut segment m into (tpw tiles per range).

@@ -169,7 +169,8 @@ struct MTile {
   u32x4 k[Geo::kKLoads];
   typename Words<Geo::kVWords>::T v[4];
   float ks, vs;
-  int rows;
+  int rows;  // rows [lo, rows) take part; the others are masked out
+  int lo;
 };
 
 // Issue the loads of one tile: `base` is the byte offset of its (block, kv
@@ -179,6 +180,7 @@ __device__ __forceinline__ void load_mtile_at(MTile<D, FP8>& t, const DecodeArgs
                                               int rows, int k_off, int v_off) {
   using Geo = MfmaGeo<D, FP8>;
   t.rows = rows;
+  t.lo = 0;
   const int nbytes = rows * Geo::kRow;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_pool + base, nbytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_pool + base, nbytes);
@@ -268,7 +270,7 @@ __device__ __forceinline__ void mfma_tile(MState<D, FP8>& st, const MTile<D, FP8
   float tm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    s[r] = (4 * g + r) < t.rows ? s[r] : -INFINITY;
+    s[r] = (4 * g + r) < t.rows && (4 * g + r) >= t.lo ? s[r] : -INFINITY;
     tm = fmaxf(tm, s[r]);
   }
   // the head's 16 tokens sit in lanes n16, n16+16, n16+32, n16+48

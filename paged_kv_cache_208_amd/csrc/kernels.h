@@ -29,6 +29,7 @@ struct DecodeArgs {
   const float* gamma_k;
   float eps, theta;
   uint32_t* counters;         // [B][Hkv] arrivals per (sequence, kv head); zero between launches
+  int window;                 // > 0: attend to the last `window` tokens only (balanced step)
 };
 
 // What a decode launch does besides attending (bit flags).

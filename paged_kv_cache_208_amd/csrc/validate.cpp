@@ -130,9 +130,9 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
                                  const float* k_scale, const float* v_scale,
                                  const int32_t* block_tables, const int32_t* context_lens, int B,
                                  int Hq, int Hkv, int D, int BS, int MBS, int64_t NB, float scale,
-                                 int kv_dtype, int partition_size, const float* gamma_q,
-                                 const float* gamma_k, float eps, float rope_theta,
-                                 const float* part_out, const float* part_max,
+                                 int kv_dtype, int partition_size, int window,
+                                 const float* gamma_q, const float* gamma_k, float eps,
+                                 float rope_theta, const float* part_out, const float* part_max,
                                  const float* part_sum, const uint32_t* counters,
                                  int max_partitions) {
   // the attention part is checked as paged_attn_decode checks partitioned work
@@ -142,7 +142,10 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
                                context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale, kv_dtype, ps_check,
                                part_out, part_max, part_sum,
                                partition_size == 0 ? MBS : max_partitions);
-  if (st != PKV_OK || B == 0) return st;
+  if (st != PKV_OK) return st;
+  if (window < 0) return PKV_EINVAL;
+  if (window > 0 && partition_size != 0) return PKV_EUNSUPPORTED;  // balanced split only
+  if (B == 0) return st;
   if (!out || !aligned(out, 16)) return PKV_EINVAL;
   if (!counters || !aligned(counters, 4)) return PKV_EINVAL;
   if (partition_size == 0) {

@@ -221,12 +221,16 @@ def generate(cfg: DecodeConfig, *, seed: int | None = None) -> dict:
     return out
 
 
-def kv_bytes(cfg: DecodeConfig, context_lens) -> int:
-    """Algorithmic KV bytes one decode step must read (K and V, plus scales)."""
-    tokens = int(np.sum(np.asarray(context_lens, dtype=np.int64)))
+def kv_bytes(cfg: DecodeConfig, context_lens, window: int = 0) -> int:
+    """Algorithmic KV bytes one decode step must read (K and V, plus scales).
+    window > 0: only each sequence's last `window` tokens are read."""
+    lens = np.asarray(context_lens, dtype=np.int64)
+    if window > 0:
+        lens = np.minimum(lens, window)
+    tokens = int(np.sum(lens))
     elem = 1 if cfg.kv_dtype == "e4m3" else 2
     b = tokens * cfg.Hkv * cfg.D * 2 * elem
     if cfg.kv_dtype == "e4m3":
-        tiles = int(np.sum(-(-np.asarray(context_lens, dtype=np.int64) // BLOCK_SIZE)))
+        tiles = int(np.sum(-(-lens // BLOCK_SIZE)))
         b += tiles * cfg.Hkv * 2 * 4
     return b

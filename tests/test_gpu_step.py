@@ -23,7 +23,7 @@ def _u16(x):
     return np.ascontiguousarray(x).view(np.uint16)
 
 
-def _step(cfg, g, ps, *, append=True, qknorm=False, splits=16):
+def _step(cfg, g, ps, *, append=True, qknorm=False, splits=16, window=0):
     """ps > 0: fixed partitions; ps == 0: balanced split into <= splits pieces."""
     B, Hq, D = g["q"].shape
     out = torch.full((B, Hq, D), float("nan"), dtype=torch.float16, device="cuda")
@@ -36,7 +36,8 @@ def _step(cfg, g, ps, *, append=True, qknorm=False, splits=16):
         kw.update(gamma_q=g["gamma_q"], gamma_k=g["gamma_k"], eps=cfg.eps, rope_theta=cfg.theta)
     _lib.paged_decode_step(out, g["q"], g["k_pool"], g["v_pool"], g["block_tables"],
                            g["context_lens"], cfg.scale, k_scale=g.get("k_scale"),
-                           v_scale=g.get("v_scale"), partition_size=ps, workspace=ws, **kw)
+                           v_scale=g.get("v_scale"), partition_size=ps, window=window,
+                           workspace=ws, **kw)
     torch.cuda.synchronize()
     return out, ws
 
@@ -260,3 +261,42 @@ def test_step_balanced_qknorm_many_sequences():
     assert torch.all(out[::7] == 0)
     assert max_abs(out, ref) <= TOL_F16
     assert torch.count_nonzero(ws[3]).item() == 0
+
+
+@pytest.mark.parametrize("window", [1, 15, 16, 17, 100, 1000])
+def test_step_sliding_window(window):
+    """Only the last `window` tokens are attended; blocks before the window
+    hold NaN here, so reading any of them would show."""
+    cfg, d = batch("c2", B=9, len_lo=1, len_hi=700, mbs=44)
+    lens = d["context_lens"]
+    kp0, vp0 = d["k_pool"].copy(), d["v_pool"].copy()
+    tab = d["block_tables"]
+    for b, L in enumerate(lens):                     # poison whole blocks before the window
+        start = max(0, int(L) - window) // 16 if window < L else 0
+        for n in range(start):
+            kp0[tab[b, n]] = np.float16(np.nan)
+            vp0[tab[b, n]] = np.float16(np.nan)
+    d2 = dict(d, k_pool=kp0, v_pool=vp0)
+    g = to_device(d2)
+    out, ws = _step(cfg, g, 0, window=window)
+    kp, vp = append_ref(kp0, vp0, d["k_new"], d["v_new"], d["slot_mapping"])
+    ref = attn_ref(d["q"], kp, vp, tab, lens, cfg.scale, window=window)
+    assert max_abs(out, ref) <= TOL_F16
+    assert torch.count_nonzero(ws[3]).item() == 0
+
+
+def test_step_sliding_window_qknorm_and_e4m3():
+    cfg, d = batch("c4", B=7, len_lo=1, len_hi=1000, mbs=63)
+    g = to_device(d)
+    out, _ = _step(cfg, g, 0, qknorm=True, window=300)
+    q2, kp, vp, _, _ = fused_append_ref(d["q"], d["k_new"], d["v_new"], d["k_pool"], d["v_pool"],
+                                        d["slot_mapping"], d["context_lens"], d["gamma_q"],
+                                        d["gamma_k"], cfg.eps, cfg.theta)
+    ref = attn_ref(q2, kp, vp, d["block_tables"], d["context_lens"], cfg.scale, window=300)
+    assert max_abs(out, ref) <= TOL_F16
+    cfg, d = batch("c5", B=6, len_lo=1, len_hi=900, mbs=57)
+    g = to_device(d)
+    out, _ = _step(cfg, g, 0, append=False, window=129)
+    ref = attn_ref(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                   cfg.scale, k_scale=d["k_scale"], v_scale=d["v_scale"], window=129)
+    assert max_abs(out, ref) <= TOL_E4M3
