@@ -37,6 +37,7 @@ from .attention import (  # noqa: F401
     attn_weights_ref,
     partials_ref,
     combine_ref,
+    mq_attn_ref,
 )
 from .e4m3 import e4m3_table, e4m3_decode  # noqa: F401
 from .append import append_ref, rmsnorm_rope_ref, fused_append_ref  # noqa: F401

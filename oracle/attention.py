@@ -189,3 +189,43 @@ def combine_ref(m, l, o, context_lens, partition_size):
             w = l[b, h, :P] * np.exp(mp - M)
             out[b, h] = (w @ o[b, h, :P]) / np.sum(w)
     return out
+
+
+def mq_attn_ref(q, k_pool, v_pool, block_tables, context_lens, scale, *,
+                k_scale=None, v_scale=None, block_size=16):
+    """Several new query tokens per sequence with a causal mask, float64.
+
+    "Roadmap: vLLM-style serving features for TornadoVM batched decode",
+    Deferred / WIP: speculative decoding verifies a batch of drafted tokens in
+    one forward (1.71 tokens per forward), and chunked prefill would put
+    several tokens of a sequence in one step.  Reading taken: q is
+    [B, nq, Hq, D]; context_lens[b] = L counts the nq new tokens, which sit
+    at positions L - nq .. L - 1; new token j attends to positions
+    0 .. L - nq + j (itself and everything before it):
+        s_t = scale * <q[b, j, h], K_b[h // g, t]>   for t <= L - nq + j,
+        out[b, j, h] = sum_t softmax(s)_t V_b[h // g, t]
+    The mask is written out on the full score vector (masked scores are
+    -inf before the softmax).  L = 0 gives zero rows; 0 < L < nq is outside
+    the contract.
+    """
+    B, nq, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    g = Hq // Hkv
+    out = np.zeros((B, nq, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        if L == 0:
+            continue
+        if L < nq:
+            raise ValueError("each sequence must hold its nq new tokens")
+        K = gather_sequence_kv(k_pool, k_scale, block_tables[b], L, block_size)
+        V = gather_sequence_kv(v_pool, v_scale, block_tables[b], L, block_size)
+        pos = np.arange(L)
+        for j in range(nq):
+            visible = pos <= L - nq + j
+            for h in range(Hq):
+                s = float(scale) * (K[h // g] @ q[b, j, h].astype(np.float64))
+                s = np.where(visible, s, -np.inf)
+                w = np.exp(s - np.max(s))
+                out[b, j, h] = (w / np.sum(w)) @ V[h // g]
+    return out

@@ -253,3 +253,30 @@ def test_sliding_window_equals_full_attention_over_the_window_only():
     for b, L in enumerate(lens):
         last = vp[tab[b, (L - 1) // 16], :, (L - 1) % 16].astype(np.float64)
         assert np.array_equal(w1[b], np.repeat(last, Hq // Hkv, axis=0))
+
+
+def test_multi_token_query_is_a_run_of_single_token_steps():
+    """Token j of nq new tokens sees exactly what a one-token decode step at
+    length L - nq + j + 1 sees; nq = 1 is plain decode; the 50-digit brute
+    force agrees on a tiny case."""
+    from oracle import mq_attn_ref
+    rng = np.random.default_rng(31)
+    Hq, Hkv, D, NB, nq = 4, 2, 16, 40, 5
+    kp = rng.standard_normal((NB, Hkv, 16, D)).astype(np.float16)
+    vp = rng.standard_normal((NB, Hkv, 16, D)).astype(np.float16)
+    lens = np.array([5, 6, 16, 17, 21, 90], dtype=np.int32)
+    tab = np.stack([rng.permutation(NB)[:6] for _ in lens]).astype(np.int32)
+    q = rng.standard_normal((len(lens), nq, Hq, D)).astype(np.float16)
+    got = mq_attn_ref(q, kp, vp, tab, lens, 0.3)
+    for j in range(nq):
+        ref = attn_ref(q[:, j], kp, vp, tab, lens - nq + j + 1, 0.3)
+        assert np.max(np.abs(got[:, j] - ref)) <= 1e-12
+    one = mq_attn_ref(q[:, :1], kp, vp, tab, lens, 0.3)[:, 0]
+    assert np.max(np.abs(one - attn_ref(q[:, 0], kp, vp, tab, lens, 0.3))) <= 1e-12
+    # brute force for the first new token of one sequence (it sees L - nq + 1 tokens)
+    b, j = 3, 0
+    L = int(lens[b]) - nq + j + 1
+    bf = attn_brute(q[b:b + 1, j], kp.astype(np.float64), vp.astype(np.float64), tab[b:b + 1],
+                    np.array([L]), 0.3)
+    bf = np.array([[float(x) for x in row] for row in bf[0]])
+    assert np.max(np.abs(got[b, j] - bf)) <= 1e-12
