@@ -69,6 +69,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=16,
                    help="most pieces one sequence is cut into by the balanced split")
+    p.add_argument("--n-query", type=int, default=1,
+                   help="new tokens per sequence (speculative verify / chunked prefill; "
+                        "balanced one-launch step only)")
     p.add_argument("--window", type=int, default=0,
                    help="sliding window in tokens (balanced one-launch step only; 0 = full)")
     p.add_argument("--unfused", action="store_true",
@@ -313,6 +316,15 @@ def main():
         bench_append_e4m3(args, cfg, d)
         return
 
+    nq = args.n_query
+    if nq > 1:
+        # several new tokens per sequence: q and the new rows get a token axis
+        rng = np.random.default_rng(208_300)
+        d = dict(d, q=rng.standard_normal((cfg.B, nq, cfg.Hq, cfg.D)).astype(np.float16),
+                 k_new=rng.standard_normal((cfg.B, nq, cfg.Hkv, cfg.D)).astype(np.float16),
+                 v_new=rng.standard_normal((cfg.B, nq, cfg.Hkv, cfg.D)).astype(np.float16))
+        args.no_cpu_baseline = True
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, d, args.cpu_seconds)
@@ -334,15 +346,16 @@ def main():
     footprint = sum(t.numel() * t.element_size() for t in base.values())
     R = args.rotate or max(2, math.ceil(ROTATE_BYTES / footprint))
     copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
-    B, Hq, D = d["q"].shape
+    B, Hq, D = d["q"].shape[0], d["q"].shape[-2], d["q"].shape[-1]
     PS = cfg.partition_size
     P = _lib.max_partitions_for(cfg.mbs, PS)
     ws = _lib.alloc_partials(B, Hq, D, P, dev) if PS else None
     # the one-launch step splits contexts evenly over all waves (partition_size 0)
     # unless --partition-size asks for fixed partitions
     step_ps = PS if args.partition_size is not None else 0
-    step_ws = _lib.alloc_step_workspace(B, Hq, cfg.Hkv, D, P if step_ps else args.splits, dev)
-    out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    step_ws = _lib.alloc_step_workspace(B, Hq * nq, cfg.Hkv, D, P if step_ps else args.splits,
+                                        dev)
+    out = torch.empty(tuple(d["q"].shape), dtype=torch.float16, device=dev)
     fp8 = cfg.kv_dtype == "e4m3"
     torch.cuda.synchronize()
 
@@ -425,7 +438,8 @@ def main():
     kv = synth.kv_bytes(cfg, d["context_lens"], args.window)
     tokens = int(d["context_lens"].astype(np.int64).sum())
     traffic = None
-    fused_balanced = not args.unfused and step_ps == 0 and args.splits == 16 and not args.window
+    fused_balanced = (not args.unfused and step_ps == 0 and args.splits == 16 and not args.window
+                      and nq == 1)
     measured = MEASURED_TRAFFIC.get((cfg.name, step_source_hash())) if fused_balanced else None
     if measured:
         traffic = measured["fetch_bytes"] + measured["write_bytes"]
@@ -457,10 +471,11 @@ def main():
                       else "append+attend+combine")),
             "launches_per_step": (3 if not fp8 else 2) if args.unfused and PS else 1,
             "window": args.window,
+            "new_tokens_per_sequence": nq,
             "rotated_copies": R,
         },
         "steps_per_s": round(1e3 / ms, 1),
-        "tokens_per_s": round(cfg.B * 1e3 / ms, 1),
+        "tokens_per_s": round(cfg.B * nq * 1e3 / ms, 1),
         "pct_hbm_peak": round(100 * value / HBM_GBPS, 2),
         "kv_bytes_per_step": kv,
         "decode_kernel_us": round(dec_avg * 1e3, 3),

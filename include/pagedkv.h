@@ -172,6 +172,17 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
  *   blocks before the window are not read.  Balanced split only
  *   (partition_size == 0, else PKV_EUNSUPPORTED); window == 0 is full
  *   attention, window < 0 is PKV_EINVAL.
+ * n_query > 1: several new tokens per sequence ("Roadmap: vLLM-style
+ *   serving features for TornadoVM batched decode", Deferred / WIP:
+ *   speculative decoding verifies drafted tokens in one forward, chunked
+ *   prefill puts several tokens of a sequence in one step).  q and out are
+ *   [B][n_query][Hq][D], k_new / v_new [B][n_query][Hkv][D]; L_b counts the
+ *   new tokens, which take positions L_b - n_query .. L_b - 1, and new token
+ *   j attends to positions 0 .. L_b - n_query + j (causal).  The tokens share
+ *   every KV byte read: they fill more columns of the same 16-wide products,
+ *   so (Hq / Hkv) * n_query must be a power of two <= 16.  Balanced split
+ *   only, no QK-norm, no window (else PKV_EUNSUPPORTED); part_* then hold
+ *   [B][n_query * Hq][max_partitions]([D]).  L_b must be 0 or >= n_query.
  * kv_dtype PKV_KV_E4M3: attend + combine only (k_new must be NULL).
  * L_b == 0: zero output row, nothing written to the pools, q untouched.
  * Errors and shape limits as for paged_attn_decode and paged_kv_append.
@@ -180,9 +191,10 @@ int paged_decode_step(void* out, void* q, const void* k_new, const void* v_new, 
                       void* v_pool, const float* k_scale, const float* v_scale,
                       const int32_t* block_tables, const int32_t* context_lens, int B, int Hq,
                       int Hkv, int D, int BS, int MBS, int64_t NB, float scale, int kv_dtype,
-                      int partition_size, int window, const float* gamma_q, const float* gamma_k,
-                      float eps, float rope_theta, float* part_out, float* part_max,
-                      float* part_sum, uint32_t* counters, int max_partitions, void* stream);
+                      int partition_size, int window, int n_query, const float* gamma_q,
+                      const float* gamma_k, float eps, float rope_theta, float* part_out,
+                      float* part_max, float* part_sum, uint32_t* counters, int max_partitions,
+                      void* stream);
 
 /*
  * paged_kv_append_e4m3 - write this step's new K/V rows into E4M3 blocks,
@@ -262,7 +274,8 @@ int pkv_validate_step(const void* out, const void* q, const void* k_new, const v
                       const float* v_scale, const int32_t* block_tables,
                       const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
                       int MBS, int64_t NB, float scale, int kv_dtype, int partition_size,
-                      int window, const float* gamma_q, const float* gamma_k, float eps,
+                      int window, int n_query, const float* gamma_q, const float* gamma_k,
+                      float eps,
                       float rope_theta, const float* part_out, const float* part_max,
                       const float* part_sum, const uint32_t* counters, int max_partitions);
 int pkv_validate_reduce(const void* out, const float* part_out, const float* part_max,

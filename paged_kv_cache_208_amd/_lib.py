@@ -36,7 +36,7 @@ _SIGNATURES = {
                                _F, _I, _I, _P, _P, _P, _I, _P]),
     "paged_attn_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
-                               _I64, _F, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I, _P]),
+                               _I64, _F, _I, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I, _P]),
     "paged_kv_copy_blocks": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I, _P]),
     "paged_kv_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P]),
     "paged_attn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
@@ -49,7 +49,7 @@ _SIGNATURES = {
     "pkv_validate_copy": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I]),
     "pkv_validate_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64]),
     "pkv_validate_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
-                               _I64, _F, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I]),
+                               _I64, _F, _I, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I]),
 }
 
 
@@ -305,16 +305,23 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
     splits contexts evenly over all waves into at most workspace-depth
     pieces; > 0 uses fixed partitions.  window > 0 attends to the last
     `window` tokens only (balanced split)."""
-    _check(out, "out", torch.float16, 3)
-    _check(q, "q", torch.float16, 3)
+    nq = 1
+    if q.dim() == 4:                      # [B, nq, Hq, D]: several new tokens per sequence
+        nq = q.shape[1]
+        q3, out3 = q.reshape(q.shape[0], -1, q.shape[3]), out.reshape(out.shape[0], -1, out.shape[3])
+    else:
+        q3, out3 = q, out
+    _check(out3, "out", torch.float16, 3)
+    _check(q3, "q", torch.float16, 3)
     kv = _kv_dtype(k_pool)
     _check(k_pool, "k_pool", k_pool.dtype, 4)
     _check(v_pool, "v_pool", k_pool.dtype, 4)
     _check(block_tables, "block_tables", torch.int32, 2)
     _check(context_lens, "context_lens", torch.int32, 1)
-    B, Hq, D = q.shape
+    B, HqN, D = q3.shape
+    Hq = HqN // nq
     NB, Hkv, BS, d2 = k_pool.shape
-    if d2 != D or v_pool.shape != k_pool.shape or tuple(out.shape) != (B, Hq, D):
+    if d2 != D or v_pool.shape != k_pool.shape or tuple(out3.shape) != (B, HqN, D):
         raise ValueError("q / out / pool shapes disagree")
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables / context_lens must have B rows")
@@ -322,10 +329,11 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
         _check(k_scale, "k_scale", torch.float32, 2)
         _check(v_scale, "v_scale", torch.float32, 2)
     if k_new is not None:
-        _check(k_new, "k_new", torch.float16, 3)
-        _check(v_new, "v_new", torch.float16, 3)
-        if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
-            raise ValueError("k_new / v_new must be [B, Hkv, D]")
+        _check(k_new, "k_new", torch.float16, 3 if nq == 1 else 4)
+        _check(v_new, "v_new", torch.float16, 3 if nq == 1 else 4)
+        want = (B, Hkv, D) if nq == 1 else (B, nq, Hkv, D)
+        if tuple(k_new.shape) != want or tuple(v_new.shape) != want:
+            raise ValueError(f"k_new / v_new must be {list(want)}")
     if gamma_k is not None:
         _check(gamma_q, "gamma_q", torch.float32, 1)
         _check(gamma_k, "gamma_k", torch.float32, 1)
@@ -335,13 +343,14 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
     _check(po, "part_out", torch.float32, 4)
     _check(ctr, "counters", torch.int32, 2)
     P = po.shape[2]
-    if (tuple(po.shape) != (B, Hq, P, D) or tuple(pm.shape) != (B, Hq, P)
-            or tuple(ps.shape) != (B, Hq, P) or tuple(ctr.shape) != (B, Hkv)):
+    if (tuple(po.shape) != (B, HqN, P, D) or tuple(pm.shape) != (B, HqN, P)
+            or tuple(ps.shape) != (B, HqN, P) or tuple(ctr.shape) != (B, Hkv)):
         raise ValueError("workspace shapes disagree")
     st = lib().paged_decode_step(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
                                  _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                                  _ptr(context_lens), B, Hq, Hkv, D, BS, block_tables.shape[1], NB,
-                                 float(scale), kv, int(partition_size), int(window), _ptr(gamma_q),
+                                 float(scale), kv, int(partition_size), int(window), nq,
+                                 _ptr(gamma_q),
                                  _ptr(gamma_k), float(eps), float(rope_theta), _ptr(po), _ptr(pm),
                                  _ptr(ps), _ptr(ctr), P, _stream(stream))
     _raise("paged_decode_step", st)

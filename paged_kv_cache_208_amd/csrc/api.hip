@@ -64,6 +64,8 @@ extern "C" int paged_attn_decode(void* out, const void* q, const void* k_pool, c
   a.part_out = part_out;
   a.part_max = part_max;
   a.part_sum = part_sum;
+  a.nq = 1;
+  a.group = Hq / Hkv;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.MBS = MBS;
@@ -91,14 +93,15 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
                                  const float* v_scale, const int32_t* block_tables,
                                  const int32_t* context_lens, int B, int Hq, int Hkv, int D,
                                  int BS, int MBS, int64_t NB, float scale, int kv_dtype,
-                                 int partition_size, int window, const float* gamma_q,
-                                 const float* gamma_k, float eps, float rope_theta,
-                                 float* part_out, float* part_max, float* part_sum,
-                                 uint32_t* counters, int max_partitions, void* stream) {
+                                 int partition_size, int window, int n_query,
+                                 const float* gamma_q, const float* gamma_k, float eps,
+                                 float rope_theta, float* part_out, float* part_max,
+                                 float* part_sum, uint32_t* counters, int max_partitions,
+                                 void* stream) {
   const int st = pkv_validate_step(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
                                    block_tables, context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale,
-                                   kv_dtype, partition_size, window, gamma_q, gamma_k, eps,
-                                   rope_theta, part_out, part_max, part_sum, counters,
+                                   kv_dtype, partition_size, window, n_query, gamma_q, gamma_k,
+                                   eps, rope_theta, part_out, part_max, part_sum, counters,
                                    max_partitions);
   if (st != PKV_OK || B == 0) return st;
   const bool fp8 = kv_dtype == PKV_KV_E4M3;
@@ -115,6 +118,8 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
   a.part_max = part_max;
   a.part_sum = part_sum;
   a.window = window;
+  a.nq = n_query;
+  a.group = Hq / Hkv;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.MBS = MBS;
@@ -132,7 +137,7 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
   if (k_new) mode |= pkv::kModeAppend;
   if (gamma_k) mode |= pkv::kModeQkNorm;
   if (partition_size == 0)  // balanced split across a fixed number of waves
-    return launch_status(pkv::launch_decode_stream(a, B, D, Hq / Hkv, fp8, mode,
+    return launch_status(pkv::launch_decode_stream(a, B, D, (Hq / Hkv) * n_query, fp8, mode,
                                                    static_cast<hipStream_t>(stream)));
   return launch_status(pkv::launch_decode_step(a, B, D, Hq / Hkv, fp8, mode,
                                                static_cast<hipStream_t>(stream)));

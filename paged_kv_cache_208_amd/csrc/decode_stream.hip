@@ -184,13 +184,20 @@ __device__ __forceinline__ Meta meta_of(const Cursor& c, const DecodeArgs& a, in
   return m;
 }
 
-template <int D, int G, bool FP8, int MODE>
+template <int D, int C, bool FP8, int MODE>
 struct StreamKernel {
   using Geo = MfmaGeo<D, FP8>;
   static constexpr bool APPEND = (MODE & kModeAppend) != 0;
   static constexpr bool QKNORM = (MODE & kModeQkNorm) != 0;
   // tiles in the load pipeline of a wave
   static constexpr int kDepth = PKV_STREAM_DEPTH;
+
+  // The C columns of a segment's 16-wide products: column col is new query
+  // token col / g of q head kvh * g + col % g (g = Hq / Hkv; one new token
+  // per sequence unless nq > 1).  Row of q and of out [B][nq][Hq][D]:
+  static __device__ __forceinline__ size_t qrow(const DecodeArgs& a, int b, int kvh, int col) {
+    return (size_t(b) * a.nq + col / a.group) * a.Hq + kvh * a.group + col % a.group;
+  }
 
   // q of head slot n16 of the segment's group, laid out as the B operand of
   // the QK products; zero past the group.  Slots past the group read outside
@@ -199,48 +206,57 @@ struct StreamKernel {
   // first tile is computed, once the loads have landed.
   static __device__ __forceinline__ void load_q(half8_t* qop, const DecodeArgs& a, int b, int kvh,
                                                 int g, int n16) {
-    const _Float16* qg = static_cast<const _Float16*>(a.q) + (size_t(b) * a.Hq + kvh * G) * D;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(qg, G * D * int(sizeof(_Float16)));
-    const int row = n16 < G ? n16 * D : G * D;
+    const size_t base = size_t(b) * a.nq * a.Hq;
+    const _Float16* qs = static_cast<const _Float16*>(a.q) + base * D;
+    const int span = a.nq * a.Hq * D;  // the sequence's q rows
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(qs, span * int(sizeof(_Float16)));
+    const int row = n16 < C ? int(qrow(a, b, kvh, n16) - base) * D : span;
 #pragma unroll
     for (int c = 0; c < Geo::kQK; ++c)
       qop[c] = __builtin_bit_cast(half8_t, buffer_load16(r, (row + qk_dim0<FP8>(c, g)) * int(sizeof(_Float16))));
   }
 
-  // Write the step's new k and v row (token L-1) of every segment whose last
-  // tile lies in the range [t0, t1), before any tile of the range is loaded.
-  // The lanes that store each piece are the ones that later load it (same
-  // lane, same address, program order: the loads observe the stores).  The
-  // loop then carries no append work.  c is the cursor of tile t0; s_cos /
-  // s_sin hold scratch angle tables (QK-norm).
-  static __device__ __forceinline__ void append_rows(const DecodeArgs& a, int B, Cursor c, int64_t t1,
-                                                     int g, int n16, int k_off, int v_off, float* s_cos,
-                                                     float* s_sin, const double* s_f,
+  // Write the step's nq new k and v rows (tokens L-nq .. L-1) of every
+  // segment into the tiles of this wave's range [t0, t1) that hold them,
+  // before any tile of the range is loaded.  The lanes that store each piece
+  // are the ones that later load it (same lane, same address, program
+  // order: the loads observe the stores); rows in tiles of another wave's
+  // range are that wave's to write.  The loop then carries no append work.
+  // c is the cursor of tile t0; s_cos / s_sin hold scratch angle tables
+  // (QK-norm, nq = 1).
+  static __device__ __forceinline__ void append_rows(const DecodeArgs& a, int B, Cursor c, int64_t t0,
+                                                     int64_t t1, int g, int n16, int k_off, int v_off,
+                                                     float* s_cos, float* s_sin, const double* s_f,
                                                      const float* s_gk) {
     using VW = typename Words<Geo::kVWords>::T;
-    while (c.S + c.T - 1 < t1) {
-      const int id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + (c.f + c.T - 1));
-      const size_t row = size_t(c.b) * a.Hkv + c.kvh;
-      const _Float16* kn = static_cast<const _Float16*>(a.k_new) + row * D;
-      const _Float16* vn = static_cast<const _Float16*>(a.v_new) + row * D;
-      half8_t kc[Geo::kKLoads];
+    while (c.S < t1) {
+      for (int i = 0; i < a.nq; ++i) {
+        const int p = c.L - a.nq + i;             // position of new token i
+        const int64_t tile = c.S + (p / 16 - c.f);
+        if (p < 0 || tile < t0 || tile >= t1) continue;
+        const int id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + p / 16);
+        const size_t row = (size_t(c.b) * a.nq + i) * a.Hkv + c.kvh;
+        const _Float16* kn = static_cast<const _Float16*>(a.k_new) + row * D;
+        const _Float16* vn = static_cast<const _Float16*>(a.v_new) + row * D;
+        half8_t kc[Geo::kKLoads];
 #pragma unroll
-      for (int i = 0; i < Geo::kKLoads; ++i)
-        kc[i] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(kn + (4 * i + g) * 8));
-      const VW vc = *reinterpret_cast<const VW*>(vn + n16 * (D / 16));
-      if constexpr (QKNORM) {
-        rope_angles<D>(s_f, s_cos, s_sin, c.L - 1);
-        norm_rope_chunks<D>(kc, s_gk, a.eps, s_cos, s_sin, g);
+        for (int k = 0; k < Geo::kKLoads; ++k)
+          kc[k] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(kn + (4 * k + g) * 8));
+        const VW vc = *reinterpret_cast<const VW*>(vn + n16 * (D / 16));
+        if constexpr (QKNORM) {
+          rope_angles<D>(s_f, s_cos, s_sin, p);
+          norm_rope_chunks<D>(kc, s_gk, a.eps, s_cos, s_sin, g);
+        }
+        const int r_new = p % 16;
+        const size_t base = (size_t(id) * a.Hkv + c.kvh) * Geo::kTile;
+        uint8_t* kt = const_cast<uint8_t*>(a.k_pool) + base;
+        uint8_t* vt = const_cast<uint8_t*>(a.v_pool) + base;
+        if (n16 == r_new)
+#pragma unroll
+          for (int k = 0; k < Geo::kKLoads; ++k)
+            *reinterpret_cast<u32x4*>(kt + k_off + k * 64) = __builtin_bit_cast(u32x4, kc[k]);
+        if (g == r_new / 4) *reinterpret_cast<VW*>(vt + v_off + (r_new % 4) * Geo::kRow) = vc;
       }
-      const int r_new = (c.L - 1) % 16;
-      const size_t base = (size_t(id) * a.Hkv + c.kvh) * Geo::kTile;
-      uint8_t* kt = const_cast<uint8_t*>(a.k_pool) + base;
-      uint8_t* vt = const_cast<uint8_t*>(a.v_pool) + base;
-      if (n16 == r_new)
-#pragma unroll
-        for (int i = 0; i < Geo::kKLoads; ++i)
-          *reinterpret_cast<u32x4*>(kt + k_off + i * 64) = __builtin_bit_cast(u32x4, kc[i]);
-      if (g == r_new / 4) *reinterpret_cast<VW*>(vt + v_off + (r_new % 4) * Geo::kRow) = vc;
       // on to the next segment
       c.n = c.T - 1;
       advance(c, a, B);
@@ -267,9 +283,9 @@ struct StreamKernel {
   // Output rows of a segment that lies inside one wave's range: o / l.
   static __device__ __forceinline__ void store_direct(const MState<D, FP8>& st, float l,
                                                       const DecodeArgs& a, int seg, int g, int n16) {
-    if (n16 >= G) return;
+    if (n16 >= C) return;
     const float inv = 1.0f / l;
-    _Float16* o = static_cast<_Float16*>(a.out) + (size_t(seg) * G + n16) * D;
+    _Float16* o = static_cast<_Float16*>(a.out) + qrow(a, seg / a.Hkv, seg % a.Hkv, n16) * D;
     typedef _Float16 hv __attribute__((ext_vector_type(Geo::kPV)));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -292,14 +308,15 @@ struct StreamKernel {
   // segment, when no other wave still needs q.
   static __device__ __forceinline__ void write_q(const DecodeArgs& a, int seg, const half8_t* qop,
                                                  int g, int n16) {
-    if (n16 >= G) return;
-    _Float16* qh = const_cast<_Float16*>(static_cast<const _Float16*>(a.q)) + (size_t(seg) * G + n16) * D;
+    if (n16 >= C) return;
+    _Float16* qh = const_cast<_Float16*>(static_cast<const _Float16*>(a.q)) +
+                   qrow(a, seg / a.Hkv, seg % a.Hkv, n16) * D;
 #pragma unroll
     for (int c = 0; c < Geo::kQK; ++c)
       *reinterpret_cast<u32x4*>(qh + qk_dim0<false>(c, g)) = __builtin_bit_cast(u32x4, qop[c]);
   }
   static __device__ __forceinline__ void stash_q(_Float16* s_q, const half8_t* qop, int g, int n16) {
-    if (n16 >= G) return;
+    if (n16 >= C) return;
 #pragma unroll
     for (int c = 0; c < Geo::kQK; ++c)
       *reinterpret_cast<u32x4*>(s_q + n16 * D + qk_dim0<false>(c, g)) = __builtin_bit_cast(u32x4, qop[c]);
@@ -309,7 +326,7 @@ struct StreamKernel {
     half8_t q[Geo::kQK];
 #pragma unroll
     for (int c = 0; c < Geo::kQK; ++c)
-      q[c] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(s_q + min(n16, G - 1) * D +
+      q[c] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(s_q + min(n16, C - 1) * D +
                                                                          qk_dim0<false>(c, g)));
     write_q(a, seg, q, g, n16);
   }
@@ -325,41 +342,43 @@ struct StreamKernel {
 
   // The last piece to arrive combines the partials and re-arms the counter.
   static __device__ __forceinline__ void finish(const DecodeArgs& a, int seg, int pieces, float* s_w) {
-    combine(a, size_t(seg) * G, pieces, s_w);
+    combine(a, seg, pieces, s_w);
     if ((threadIdx.x & (kWave - 1)) == 0)
       __hip_atomic_store(a.counters + seg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // Float4 pieces of one partial (G rows of D) and how many each lane owns.
-  static constexpr int kF4 = G * D / 4;
+  // Float4 pieces of one partial (C rows of D) and how many each lane owns.
+  static constexpr int kF4 = C * D / 4;
   static constexpr int kOwn = (kF4 + kWave - 1) / kWave;
 
-  // Buffer over the G partial rows of output row0 (all partitions).
+  // Buffer over the C partial rows of output row0 (all partitions).
   static __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rows(const DecodeArgs& a,
                                                                         size_t row0) {
     const size_t stride = size_t(a.max_partitions) * D;
-    return make_rsrc(a.part_out + row0 * stride, int(G * stride * sizeof(float)));
+    return make_rsrc(a.part_out + row0 * stride, int(C * stride * sizeof(float)));
   }
   static __device__ __forceinline__ int partial_offset(const DecodeArgs& a, int c, int j) {
     return int(((4 * c / D) * size_t(a.max_partitions) * D + size_t(j) * D + 4 * c % D) *
                sizeof(float));
   }
 
-  // A piece's partial, kept in LDS until it is written out: o / l of the G
-  // rows (G * D floats), then the G maxima (natural-log units) and G sums.
-  static constexpr int kStage = G * D + 2 * G;
+  // A piece's partial, kept in LDS until it is written out: o / l of the C
+  // rows (C * D floats), then the C maxima (natural-log units) and C sums.
+  static constexpr int kStage = C * D + 2 * C;
 
   static __device__ __forceinline__ void stage_partial(const MState<D, FP8>& st, float l, int g,
                                                        int n16, float* s_o) {
-    if (n16 >= G) return;
-    const float inv = 1.0f / l;
+    if (n16 >= C) return;
+    // a causal column can see no token of a piece (l = 0): its o is 0 and
+    // its weight in the combine exp(m - M) l is 0
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int i = 0; i < Geo::kPV; ++i) s_o[n16 * D + (4 * g + r) * Geo::kPV + i] = st.acc[i][r] * inv;
     if (g == 0) {
-      s_o[G * D + n16] = st.m * kLn2;
-      s_o[G * D + G + n16] = l;
+      s_o[C * D + n16] = st.m * kLn2;
+      s_o[C * D + C + n16] = l;
     }
   }
 
@@ -375,30 +394,31 @@ struct StreamKernel {
       if (c < kF4)
         store16_coherent(rs, partial_offset(a, c, j), *reinterpret_cast<const u32x4*>(s_o + 4 * c));
     }
-    if (lane < G) {
+    if (lane < C) {
       const size_t pr = (row0 + lane) * a.max_partitions + j;
-      store_f32<true>(a.part_max + pr, s_o[G * D + lane]);
-      store_f32<true>(a.part_sum + pr, s_o[G * D + G + lane]);
+      store_f32<true>(a.part_max + pr, s_o[C * D + lane]);
+      store_f32<true>(a.part_sum + pr, s_o[C * D + C + lane]);
     }
   }
 
-  // Log-sum-exp combine of `pieces` partials of the G heads starting at
-  // output row row0 (one wave; weights staged in LDS).  A lane owns float4
-  // pieces of the G rows and keeps a batch of partials' loads in flight.
-  static __device__ __forceinline__ void combine(const DecodeArgs& a, size_t row0, int pieces,
+  // Log-sum-exp combine of the `pieces` partials of segment seg's C columns
+  // (one wave; weights staged in LDS).  A lane owns float4 pieces of the C
+  // rows and keeps a batch of partials' loads in flight.
+  static __device__ __forceinline__ void combine(const DecodeArgs& a, int seg, int pieces,
                                                  float* s_w) {
     const int lane = threadIdx.x & (kWave - 1);
+    const size_t row0 = size_t(seg) * C;  // the segment's partial rows
     constexpr int kBatch = kOwn >= 16 ? 1 : 16 / kOwn;
     const __amdgpu_buffer_rsrc_t rs = partial_rows(a, row0);
     // all loads of the statistics and of the first batch of partial rows go
     // out together: one round trip when pieces <= kBatch
-    constexpr int kStat = (G * kMaxStepPartitions + kWave - 1) / kWave;
+    constexpr int kStat = (C * kMaxStepPartitions + kWave - 1) / kWave;
     float mv[kStat], lv[kStat];
 #pragma unroll
     for (int i = 0; i < kStat; ++i) {
       const int t = lane + i * kWave;
       mv[i] = lv[i] = 0.0f;
-      if (t < G * pieces) {
+      if (t < C * pieces) {
         const size_t pr = (row0 + t / pieces) * a.max_partitions + t % pieces;
         mv[i] = load_f32_coherent(a.part_max + pr);
         lv[i] = load_f32_coherent(a.part_sum + pr);
@@ -419,13 +439,13 @@ struct StreamKernel {
 #pragma unroll
     for (int i = 0; i < kStat; ++i) {
       const int t = lane + i * kWave;
-      if (t < G * pieces) {
+      if (t < C * pieces) {
         const int j = t / pieces, p = t % pieces;
         s_w[2 * (j * kMaxStepPartitions + p)] = mv[i];
         s_w[2 * (j * kMaxStepPartitions + p) + 1] = lv[i];
       }
     }
-    for (int j = lane; j < G; j += kWave) {
+    for (int j = lane; j < C; j += kWave) {
       float* w = s_w + 2 * j * kMaxStepPartitions;
       float M = -FLT_MAX;
       for (int p = 0; p < pieces; ++p) M = fmaxf(M, w[2 * p]);
@@ -462,33 +482,35 @@ struct StreamKernel {
         half4_t o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = (_Float16)(num[k][e] / den);
-        *reinterpret_cast<half4_t*>(static_cast<_Float16*>(a.out) + (row0 + h) * D + 4 * c % D) = o;
+        *reinterpret_cast<half4_t*>(static_cast<_Float16*>(a.out) +
+                                    qrow(a, seg / a.Hkv, seg % a.Hkv, h) * D + 4 * c % D) = o;
       }
     }
   }
 };
 
-template <int D, int G, bool FP8, int MODE>
+template <int D, int C, bool FP8, int MODE>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<FP8>(), 8)))
 void decode_stream_kernel(DecodeArgs a, int B, int workers) {
-  using K = StreamKernel<D, G, FP8, MODE>;
+  using K = StreamKernel<D, C, FP8, MODE>;
   using Geo = MfmaGeo<D, FP8>;
-  static_assert(G <= 16, "head slots of one 16-wide product");
+  static_assert(C <= 16, "head slots of one 16-wide product");
   const int lane = threadIdx.x;
   const int worker = blockIdx.x;
   const int g = lane / 16;
   const int n16 = lane % 16;
   const int k_off = n16 * Geo::kRow + g * 16;
   const int v_off = (4 * g) * Geo::kRow + n16 * Geo::kVBytes;
+  const int jcol = n16 < C ? n16 / a.group : 0;  // new query token of this lane's column
 
-  __shared__ float s_w[2 * G * kMaxStepPartitions];  // combine weights
+  __shared__ float s_w[2 * C * kMaxStepPartitions];  // combine weights
   __shared__ float s_fin[K::kStage];                  // the range's last piece
   __shared__ float s_pend[K::kStage];                 // a piece that ended earlier
   // rotation angles of two segments' positions: the segment being computed
   // and the next one being prepared (QK-norm modes)
   __shared__ float s_cos[K::QKNORM ? 2 * (D / 2) : 1];
   __shared__ float s_sin[K::QKNORM ? 2 * (D / 2) : 1];
-  __shared__ _Float16 s_q[K::QKNORM ? G * D : 1];
+  __shared__ _Float16 s_q[K::QKNORM ? C * D : 1];
   __shared__ double s_f[K::QKNORM ? D / 2 : 1];      // rotation frequencies
   __shared__ float s_gq[K::QKNORM ? D : 1];          // RMSNorm weights of q and k
   __shared__ float s_gk[K::QKNORM ? D : 1];
@@ -515,7 +537,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       }
     }
     if constexpr (K::APPEND)
-      K::append_rows(a, B, cur, t1, g, n16, k_off, v_off, s_cos, s_sin, s_f, s_gk);
+      K::append_rows(a, B, cur, t0, t1, g, n16, k_off, v_off, s_cos, s_sin, s_f, s_gk);
     auto prepare_segment = [&](Meta& m) {
       m.slot = ord++ & 1;
       if constexpr (K::QKNORM) {
@@ -604,7 +626,10 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
                               s_sin + mx.slot * (D / 2), g);
       }
       issue_fence();
-      mfma_tile<D, FP8>(st, x, qop, a.scale_log2, g);
+      // causal limit of this lane's column: new token j sees positions up to
+      // L - nq + j (rows of tile f + n at or past the limit are masked)
+      const int col_hi = mx.L - a.nq + 1 + jcol - 16 * (mx.f + mx.n);
+      mfma_tile<D, FP8>(st, x, qop, a.scale_log2, g, col_hi);
       if (t + 1 >= t1) {
         mfin = mx;
         return;
@@ -647,9 +672,9 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       if constexpr (K::QKNORM) K::write_q(a, fseg, qop, g, n16);
     } else {
       K::stage_partial(st, l, g, n16, s_fin);
-      K::write_partial(a, size_t(fseg) * G, int(worker - mf.S / tpw), s_fin);
+      K::write_partial(a, size_t(fseg) * C, int(worker - mf.S / tpw), s_fin);
     }
-    if (pend) K::write_partial(a, size_t(pseg) * G, pj, s_pend);
+    if (pend) K::write_partial(a, size_t(pseg) * C, pj, s_pend);
     if (pend || fpieces > 1) {
       __builtin_amdgcn_s_waitcnt(0);  // partials at device scope
       const uint32_t pprev = pend ? K::arrive(a, pseg) : 0u;
@@ -668,8 +693,8 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   // sequences with no tokens: zero output rows, one wave each
   for (int b = worker; b < B; b += workers)
     if (load_uniform(a.context_lens + b) == 0)
-      for (int i = lane; i < a.Hq * D; i += kWave)
-        static_cast<_Float16*>(a.out)[size_t(b) * a.Hq * D + i] = (_Float16)0.0f;
+      for (int i = lane; i < a.nq * a.Hq * D; i += kWave)
+        static_cast<_Float16*>(a.out)[size_t(b) * a.nq * a.Hq * D + i] = (_Float16)0.0f;
 }
 
 // Compute units of the current device (queried once per device).
@@ -687,50 +712,54 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int D, int G, bool FP8, int MODE>
+template <int D, int C, bool FP8, int MODE>
 hipError_t launch_stream(const DecodeArgs& a, int B, hipStream_t stream) {
   const int workers = device_cus() * 4 * stream_waves_per_eu<FP8>();
-  hipLaunchKernelGGL((decode_stream_kernel<D, G, FP8, MODE>), dim3(workers), dim3(kWave), 0, stream,
+  hipLaunchKernelGGL((decode_stream_kernel<D, C, FP8, MODE>), dim3(workers), dim3(kWave), 0, stream,
                      a, B, workers);
   return hipGetLastError();
 }
 
-template <int D, int G, bool FP8>
+template <int D, int C, bool FP8>
 hipError_t launch_stream_mode(const DecodeArgs& a, int B, int mode, hipStream_t stream) {
   if constexpr (FP8) {
-    if (mode == kModeCombine) return launch_stream<D, G, true, kModeCombine>(a, B, stream);
+    if (mode == kModeCombine) return launch_stream<D, C, true, kModeCombine>(a, B, stream);
     return hipErrorInvalidValue;
   } else {
     switch (mode) {
-      case kModeCombine: return launch_stream<D, G, false, kModeCombine>(a, B, stream);
+      case kModeCombine: return launch_stream<D, C, false, kModeCombine>(a, B, stream);
       case kModeAppend | kModeCombine:
-        return launch_stream<D, G, false, kModeAppend | kModeCombine>(a, B, stream);
+        return launch_stream<D, C, false, kModeAppend | kModeCombine>(a, B, stream);
       case kModeAppend | kModeQkNorm | kModeCombine:
-        return launch_stream<D, G, false, kModeAppend | kModeQkNorm | kModeCombine>(a, B, stream);
+        // QK-norm runs with one new token per sequence: at most 8 columns
+        if constexpr (C <= 8)
+          return launch_stream<D, C, false, kModeAppend | kModeQkNorm | kModeCombine>(a, B, stream);
+        return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
   }
 }
 
 template <int D, bool FP8>
-hipError_t launch_stream_group(const DecodeArgs& a, int B, int group, int mode, hipStream_t stream) {
-  switch (group) {
+hipError_t launch_stream_cols(const DecodeArgs& a, int B, int cols, int mode, hipStream_t stream) {
+  switch (cols) {
     case 1: return launch_stream_mode<D, 1, FP8>(a, B, mode, stream);
     case 2: return launch_stream_mode<D, 2, FP8>(a, B, mode, stream);
     case 4: return launch_stream_mode<D, 4, FP8>(a, B, mode, stream);
     case 8: return launch_stream_mode<D, 8, FP8>(a, B, mode, stream);
+    case 16: return launch_stream_mode<D, 16, FP8>(a, B, mode, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_stream(const DecodeArgs& a, int B, int D, int group, bool fp8, int mode,
+hipError_t launch_decode_stream(const DecodeArgs& a, int B, int D, int cols, bool fp8, int mode,
                                 hipStream_t stream) {
-  if (D == 128) return fp8 ? launch_stream_group<128, true>(a, B, group, mode, stream)
-                           : launch_stream_group<128, false>(a, B, group, mode, stream);
-  if (D == 64) return fp8 ? launch_stream_group<64, true>(a, B, group, mode, stream)
-                          : launch_stream_group<64, false>(a, B, group, mode, stream);
+  if (D == 128) return fp8 ? launch_stream_cols<128, true>(a, B, cols, mode, stream)
+                           : launch_stream_cols<128, false>(a, B, cols, mode, stream);
+  if (D == 64) return fp8 ? launch_stream_cols<64, true>(a, B, cols, mode, stream)
+                          : launch_stream_cols<64, false>(a, B, cols, mode, stream);
   return hipErrorInvalidValue;
 }
 

@@ -260,7 +260,8 @@ struct MState {
 
 template <int D, bool FP8>
 __device__ __forceinline__ void mfma_tile(MState<D, FP8>& st, const MTile<D, FP8>& t,
-                                          const half8_t* qop, float scale_log2, int g) {
+                                          const half8_t* qop, float scale_log2, int g,
+                                          int col_hi = 16) {
   using Geo = MfmaGeo<D, FP8>;
   float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -270,7 +271,7 @@ __device__ __forceinline__ void mfma_tile(MState<D, FP8>& st, const MTile<D, FP8
   float tm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    s[r] = (4 * g + r) < t.rows && (4 * g + r) >= t.lo ? s[r] : -INFINITY;
+    s[r] = (4 * g + r) < min(t.rows, col_hi) && (4 * g + r) >= t.lo ? s[r] : -INFINITY;
     tm = fmaxf(tm, s[r]);
   }
   // the head's 16 tokens sit in lanes n16, n16+16, n16+32, n16+48

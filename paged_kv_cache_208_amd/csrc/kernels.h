@@ -30,6 +30,8 @@ struct DecodeArgs {
   float eps, theta;
   uint32_t* counters;         // [B][Hkv] arrivals per (sequence, kv head); zero between launches
   int window;                 // > 0: attend to the last `window` tokens only (balanced step)
+  int nq;                     // new query tokens per sequence (balanced step; 1 otherwise)
+  int group;                  // Hq / Hkv
 };
 
 // What a decode launch does besides attending (bit flags).
@@ -93,7 +95,8 @@ hipError_t launch_decode(const DecodeArgs& a, int B, int D, int group, bool fp8,
                          DecodeEngine engine, hipStream_t stream);
 hipError_t launch_decode_step(const DecodeArgs& a, int B, int D, int group, bool fp8, int mode,
                               hipStream_t stream);
-hipError_t launch_decode_stream(const DecodeArgs& a, int B, int D, int group, bool fp8, int mode,
+// cols = (Hq / Hkv) * nq, the used columns of the 16-wide products (1..16)
+hipError_t launch_decode_stream(const DecodeArgs& a, int B, int D, int cols, bool fp8, int mode,
                                 hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int B, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int T, int D, bool fused, hipStream_t stream);

@@ -130,7 +130,7 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
                                  const float* k_scale, const float* v_scale,
                                  const int32_t* block_tables, const int32_t* context_lens, int B,
                                  int Hq, int Hkv, int D, int BS, int MBS, int64_t NB, float scale,
-                                 int kv_dtype, int partition_size, int window,
+                                 int kv_dtype, int partition_size, int window, int n_query,
                                  const float* gamma_q, const float* gamma_k, float eps,
                                  float rope_theta, const float* part_out, const float* part_max,
                                  const float* part_sum, const uint32_t* counters,
@@ -145,6 +145,14 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
   if (st != PKV_OK) return st;
   if (window < 0) return PKV_EINVAL;
   if (window > 0 && partition_size != 0) return PKV_EUNSUPPORTED;  // balanced split only
+  if (n_query < 1) return PKV_EINVAL;
+  if (n_query > 1) {
+    // several new tokens: balanced split, (Hq / Hkv) * n_query <= 16 columns,
+    // neither QK-norm nor a window
+    if (partition_size != 0 || window != 0 || gamma_k != nullptr) return PKV_EUNSUPPORTED;
+    const int cols = (Hq / Hkv) * n_query;
+    if (cols > 16 || (cols & (cols - 1)) != 0) return PKV_EUNSUPPORTED;
+  }
   if (B == 0) return st;
   if (!out || !aligned(out, 16)) return PKV_EINVAL;
   if (!counters || !aligned(counters, 4)) return PKV_EINVAL;

@@ -171,7 +171,8 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 def _step_args(**kw):
     a = dict(out=A, q=A, k_new=A, v_new=A, k_pool=A, v_pool=A, k_scale=None, v_scale=None,
              block_tables=A, context_lens=A, B=2, Hq=8, Hkv=2, D=128, BS=16, MBS=8, NB=100,
-             scale=0.1, kv_dtype=0, partition_size=64, window=0, gamma_q=None, gamma_k=None,
+             scale=0.1, kv_dtype=0, partition_size=64, window=0, n_query=1, gamma_q=None,
+             gamma_k=None,
              eps=1e-6,
              theta=1e6, part_out=A, part_max=A, part_sum=A, counters=A, max_partitions=2)
     a.update(kw)
@@ -184,6 +185,13 @@ def _step_args(**kw):
     (dict(partition_size=0, max_partitions=16, window=100), 0),
     (dict(partition_size=0, max_partitions=16, window=-1), -1),
     (dict(window=100), -2),
+    (dict(n_query=0), -1),
+    (dict(n_query=2), -2),
+    (dict(partition_size=0, max_partitions=16, n_query=4), 0),
+    (dict(partition_size=0, max_partitions=16, n_query=3), -2),
+    (dict(partition_size=0, max_partitions=16, n_query=8), -2),
+    (dict(partition_size=0, max_partitions=16, n_query=2, window=64), -2),
+    (dict(partition_size=0, max_partitions=16, n_query=2, gamma_k=A, gamma_q=A), -2),
     (dict(partition_size=0, max_partitions=2), -1),
     (dict(partition_size=0, max_partitions=65), -2),
     (dict(partition_size=0, part_out=None), -1),
