@@ -32,7 +32,11 @@
  *   part_sum     [B][Hq][P]          fp32
  * q head h reads kv head h / (Hq / Hkv) (contiguous GQA groups).
  *
- * Supported shapes: D in {64, 128}; BS == 16; Hq % Hkv == 0 with
+ * Supported shapes: D in {64, 128}; BS == 16, and BS == 32 also for
+ * paged_kv_append, paged_kv_append_e4m3, paged_kv_copy_blocks and the
+ * balanced paged_decode_step ("Distributed LLM Inference Serving
+ * Platform", section 12: 16 or 32 tokens per physical block; the kernels
+ * read a 32-token block as two 16-token tiles); Hq % Hkv == 0 with
  * Hq / Hkv in {1, 2, 4, 8}; partition_size 0 or a positive multiple of 16
  * no larger than 16384; MBS * BS <= 2^24.
  *

@@ -3,6 +3,7 @@
 #include "pagedkv.h"
 #include "kernels.h"
 #include "device.h"
+#include "shape_limits.h"
 
 #include <cstdlib>
 #include <cstring>
@@ -35,7 +36,7 @@ extern "C" int paged_kv_append(const void* k_new, const void* v_new, void* k_poo
   const bool fused = gamma_k != nullptr;
   pkv::AppendArgs a{k_new, v_new, k_pool, v_pool, slot_mapping,
                     fused ? q_inout : nullptr, fused ? gamma_q : nullptr, gamma_k,
-                    fused ? context_lens : nullptr, fused ? Hq : 0, Hkv, eps, rope_theta};
+                    fused ? context_lens : nullptr, fused ? Hq : 0, Hkv, eps, rope_theta, BS};
   return launch_status(pkv::launch_append(a, T, D, fused, static_cast<hipStream_t>(stream)));
 }
 
@@ -64,6 +65,7 @@ extern "C" int paged_attn_decode(void* out, const void* q, const void* k_pool, c
   a.part_out = part_out;
   a.part_max = part_max;
   a.part_sum = part_sum;
+  a.bs_tiles = 1;
   a.nq = 1;
   a.group = Hq / Hkv;
   a.Hq = Hq;
@@ -118,6 +120,7 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
   a.part_max = part_max;
   a.part_sum = part_sum;
   a.window = window;
+  a.bs_tiles = BS / pkv::kBlockSize;
   a.nq = n_query;
   a.group = Hq / Hkv;
   a.Hq = Hq;
@@ -164,6 +167,6 @@ extern "C" int paged_kv_append_e4m3(const void* k_new, const void* v_new, void* 
                                           slot_mapping, T, Hkv, D, BS, NB);
   if (st != PKV_OK || T == 0) return st;
   pkv::AppendE4m3Args a{k_new, v_new, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
-                        k_scale, v_scale, slot_mapping, Hkv};
+                        k_scale, v_scale, slot_mapping, Hkv, BS};
   return launch_status(pkv::launch_append_e4m3(a, T, D, static_cast<hipStream_t>(stream)));
 }

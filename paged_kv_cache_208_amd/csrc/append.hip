@@ -2,7 +2,8 @@
 //
 // Plain scatter ("Distributed LLM Inference Serving Platform", section
 // 5.1): token i's K and V rows go to pool slot s = slot_mapping[i], i.e.
-// block s / 16, row s % 16 of every kv head's tile; s < 0 skips the token.
+// block s / BS, row s % BS of every kv head's rows (BS = 16 or 32 tokens per
+// block); s < 0 skips the token.
 //
 // Fused Qwen3 prologue ("Roadmap: vLLM-style serving features for TornadoVM
 // batched decode", Core batched decode): before the scatter, every q head
@@ -24,15 +25,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int t = blockIdx.x;
   const int64_t slot = a.slot_mapping[t];
   if (slot < 0) return;
-  const int64_t blk = slot / 16;
-  const int row = int(slot % 16);
+  const int64_t blk = slot / a.bs;
+  const int row = int(slot % a.bs);
   constexpr int CPH = D / 8;  // 16-byte chunks per head row
   const int chunks = a.Hkv * CPH;
   for (int i = threadIdx.x; i < chunks; i += kAppendThreads) {
     const int h = i / CPH;
     const int cc = i % CPH;
     const size_t src = (size_t(t) * a.Hkv + h) * D + cc * 8;
-    const size_t dst = ((size_t(blk) * a.Hkv + h) * 16 + row) * D + cc * 8;
+    const size_t dst = ((size_t(blk) * a.Hkv + h) * a.bs + row) * D + cc * 8;
     const u32x4 kx = *reinterpret_cast<const u32x4*>(static_cast<const _Float16*>(a.k_new) + src);
     const u32x4 vx = *reinterpret_cast<const u32x4*>(static_cast<const _Float16*>(a.v_new) + src);
     *reinterpret_cast<u32x4*>(static_cast<_Float16*>(a.k_pool) + dst) = kx;
@@ -69,8 +70,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_fused_kernel(AppendArgs
   const bool upper = c >= LPH / 2;
   const int pair0 = (c % (LPH / 2)) * 8;  // pair index of this lane's first element
   const int nheads = a.Hq + 2 * a.Hkv;
-  const int64_t blk = slot / 16;
-  const int row = int(slot % 16);
+  const int64_t blk = slot / a.bs;
+  const int row = int(slot % a.bs);
 
   for (int hh = (threadIdx.x / kWave) * HPW + lane / LPH; hh < nheads; hh += HPB) {
     const _Float16* src;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_fused_kernel(AppendArgs
       src = static_cast<const _Float16*>(is_k ? a.k_new : a.v_new) + (size_t(t) * a.Hkv + h) * D;
       dst = slot < 0 ? nullptr
                      : static_cast<_Float16*>(is_k ? a.k_pool : a.v_pool) +
-                           ((size_t(blk) * a.Hkv + h) * 16 + row) * D;
+                           ((size_t(blk) * a.Hkv + h) * a.bs + row) * D;
       if (is_k) gamma = a.gamma_k;
     }
     const u32x4 raw = *reinterpret_cast<const u32x4*>(src + c * 8);

@@ -13,7 +13,7 @@
 //
 // One wave per (token, kv head, pool): the new row is D fp16 values (one or
 // two per lane), the block's earlier rows r * D bytes (four per lane per
-// pass).
+// pass); blocks of 16 or 32 tokens.
 #include "device.h"
 #include "kernels.h"
 
@@ -37,9 +37,9 @@ __global__ __launch_bounds__(kWave) void append_e4m3_kernel(AppendE4m3Args a) {
   const int lane = threadIdx.x;
   const int64_t slot = a.slot_mapping[t];
   if (slot < 0) return;
-  const int64_t n = slot / 16;
-  const int r = int(slot % 16);
-  uint8_t* tile = (is_v ? a.v_pool : a.k_pool) + (size_t(n) * a.Hkv + h) * 16 * D;
+  const int64_t n = slot / a.bs;
+  const int r = int(slot % a.bs);
+  uint8_t* tile = (is_v ? a.v_pool : a.k_pool) + (size_t(n) * a.Hkv + h) * a.bs * D;
   float* scale = (is_v ? a.v_scale : a.k_scale) + size_t(n) * a.Hkv + h;
   const _Float16* x = static_cast<const _Float16*>(is_v ? a.v_new : a.k_new) + (size_t(t) * a.Hkv + h) * D;
 

@@ -159,6 +159,7 @@ struct Meta {
   int b, kvh, n, L, T, f;
   int lo;      // rows of the tile before the window (first tile only)
   int id;      // physical block of the tile
+  int half;    // which 16-token tile of a 32-token block
   int slot;    // angle table of the segment (QK-norm modes)
   int64_t S;
   bool first;  // first tile of the wave's piece of the segment
@@ -169,7 +170,8 @@ __device__ __forceinline__ Meta meta_of(const Cursor& c, const DecodeArgs& a, in
                                         int64_t t1) {
   Meta m;
   // a scalar load; its result is first needed one loop step later
-  m.id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + c.f + c.n);
+  m.id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + (c.f + c.n) / a.bs_tiles);
+  m.half = (c.f + c.n) % a.bs_tiles;
   m.slot = 0;
   m.f = c.f;
   m.lo = c.n == 0 ? window_start(c.L, a.window) - 16 * c.f : 0;
@@ -234,7 +236,7 @@ struct StreamKernel {
         const int p = c.L - a.nq + i;             // position of new token i
         const int64_t tile = c.S + (p / 16 - c.f);
         if (p < 0 || tile < t0 || tile >= t1) continue;
-        const int id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + p / 16);
+        const int id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + p / 16 / a.bs_tiles);
         const size_t row = (size_t(c.b) * a.nq + i) * a.Hkv + c.kvh;
         const _Float16* kn = static_cast<const _Float16*>(a.k_new) + row * D;
         const _Float16* vn = static_cast<const _Float16*>(a.v_new) + row * D;
@@ -248,7 +250,8 @@ struct StreamKernel {
           norm_rope_chunks<D>(kc, s_gk, a.eps, s_cos, s_sin, g);
         }
         const int r_new = p % 16;
-        const size_t base = (size_t(id) * a.Hkv + c.kvh) * Geo::kTile;
+        const size_t base = ((size_t(id) * a.Hkv + c.kvh) * a.bs_tiles + (p / 16) % a.bs_tiles) *
+                            Geo::kTile;
         uint8_t* kt = const_cast<uint8_t*>(a.k_pool) + base;
         uint8_t* vt = const_cast<uint8_t*>(a.v_pool) + base;
         if (n16 == r_new)
@@ -270,7 +273,8 @@ struct StreamKernel {
   // wait before the products stays partial on every path.
   static __device__ __forceinline__ void issue(MTile<D, FP8>& t, const DecodeArgs& a, const Meta& m,
                                                bool live, int k_off, int v_off) {
-    const size_t base = live ? (size_t(m.id) * a.Hkv + m.kvh) * Geo::kTile : 0;
+    const size_t base =
+        live ? ((size_t(m.id) * a.Hkv + m.kvh) * a.bs_tiles + m.half) * Geo::kTile : 0;
     load_mtile_at<D, FP8>(t, a, base, live ? min(16, m.L - 16 * (m.f + m.n)) : 0, k_off, v_off);
     t.lo = live ? m.lo : 0;
   }

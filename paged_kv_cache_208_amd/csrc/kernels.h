@@ -32,6 +32,7 @@ struct DecodeArgs {
   int window;                 // > 0: attend to the last `window` tokens only (balanced step)
   int nq;                     // new query tokens per sequence (balanced step; 1 otherwise)
   int group;                  // Hq / Hkv
+  int bs_tiles;               // 16-token tiles per block: 1, or 2 for 32-token blocks
 };
 
 // What a decode launch does besides attending (bit flags).
@@ -63,6 +64,7 @@ struct AppendArgs {
   const int32_t* context_lens;  // [T], fused only
   int Hq, Hkv;
   float eps, theta;
+  int bs;                     // tokens per block (16 or 32)
 };
 
 struct AppendE4m3Args {
@@ -74,6 +76,7 @@ struct AppendE4m3Args {
   float* v_scale;
   const int64_t* slot_mapping;  // [T]
   int Hkv;
+  int bs;                     // tokens per block (16 or 32)
 };
 
 struct CopyArgs {

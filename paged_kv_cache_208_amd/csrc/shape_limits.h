@@ -3,7 +3,8 @@
 #include <cstdint>
 
 namespace pkv {
-constexpr int kBlockSize = 16;            // tokens per physical KV block
+constexpr int kBlockSize = 16;            // tokens per physical KV block (and per tile)
+constexpr int kBlockSizeLarge = 32;       // the other block size some entry points take
 constexpr int kPartitionQuantum = 16;     // partition sizes are whole blocks
 constexpr int kMaxPartition = 16384;      // tokens per split-context partition
 constexpr int64_t kMaxContext = int64_t(1) << 24;   // MBS * BS

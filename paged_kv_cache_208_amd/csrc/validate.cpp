@@ -17,6 +17,9 @@ bool supported_head_dim(int D) { return D == 64 || D == 128; }
 
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
+// Block sizes of the entry points that take either (the rest take 16 only).
+bool supported_block_size(int BS) { return BS == pkv::kBlockSize || BS == pkv::kBlockSizeLarge; }
+
 }  // namespace
 
 extern "C" const char* pkv_strerror(int status) {
@@ -44,7 +47,7 @@ extern "C" int pkv_validate_append(const void* k_new, const void* v_new, const v
                                    const int32_t* context_lens, float eps, float rope_theta) {
   if (T < 0 || Hkv <= 0 || NB <= 0 || D <= 0 || BS <= 0) return PKV_EINVAL;
   if (!supported_head_dim(D)) return PKV_EUNSUPPORTED;
-  if (BS != pkv::kBlockSize) return PKV_EUNSUPPORTED;
+  if (!supported_block_size(BS)) return PKV_EUNSUPPORTED;
   if (int64_t(T) * Hkv > pkv::kMaxAppendRows) return PKV_EUNSUPPORTED;
   if (T == 0) return PKV_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping) return PKV_EINVAL;
@@ -135,13 +138,18 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
                                  float rope_theta, const float* part_out, const float* part_max,
                                  const float* part_sum, const uint32_t* counters,
                                  int max_partitions) {
+  // 32-token blocks: balanced split only; they are checked as 16-token
+  // tiles (two per block) from here on
+  if (!supported_block_size(BS)) return PKV_EUNSUPPORTED;
+  if (BS != pkv::kBlockSize && partition_size != 0) return PKV_EUNSUPPORTED;
+  const int tiles = BS / pkv::kBlockSize;
   // the attention part is checked as paged_attn_decode checks partitioned work
   // (partition_size 0 here means a balanced split, which needs the same workspace)
-  const int ps_check = partition_size == 0 ? BS : partition_size;
+  const int ps_check = partition_size == 0 ? pkv::kBlockSize : partition_size;
   int st = pkv_validate_decode(out, q, k_pool, v_pool, k_scale, v_scale, block_tables,
-                               context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale, kv_dtype, ps_check,
-                               part_out, part_max, part_sum,
-                               partition_size == 0 ? MBS : max_partitions);
+                               context_lens, B, Hq, Hkv, D, pkv::kBlockSize, MBS * tiles,
+                               NB * tiles, scale, kv_dtype, ps_check, part_out, part_max, part_sum,
+                               partition_size == 0 ? MBS * tiles : max_partitions);
   if (st != PKV_OK) return st;
   if (window < 0) return PKV_EINVAL;
   if (window > 0 && partition_size != 0) return PKV_EUNSUPPORTED;  // balanced split only
@@ -187,7 +195,7 @@ extern "C" int pkv_validate_copy(const void* k_pool, const void* v_pool, const f
   if (n < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB <= 0) return PKV_EINVAL;
   if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_E4M3) return PKV_EINVAL;
   if (!supported_head_dim(D)) return PKV_EUNSUPPORTED;
-  if (BS != pkv::kBlockSize) return PKV_EUNSUPPORTED;
+  if (!supported_block_size(BS)) return PKV_EUNSUPPORTED;
   if (int64_t(n) > pkv::kMaxGrid) return PKV_EUNSUPPORTED;
   if (n == 0) return PKV_OK;
   if (!k_pool || !v_pool || !src || !dst) return PKV_EINVAL;
@@ -206,7 +214,7 @@ extern "C" int pkv_validate_append_e4m3(const void* k_new, const void* v_new, co
                                         int Hkv, int D, int BS, int64_t NB) {
   if (T < 0 || Hkv <= 0 || NB <= 0 || D <= 0 || BS <= 0) return PKV_EINVAL;
   if (!supported_head_dim(D)) return PKV_EUNSUPPORTED;
-  if (BS != pkv::kBlockSize) return PKV_EUNSUPPORTED;
+  if (!supported_block_size(BS)) return PKV_EUNSUPPORTED;
   if (int64_t(T) > pkv::kMaxGrid || Hkv > 65535) return PKV_EUNSUPPORTED;
   if (T == 0) return PKV_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale || !slot_mapping)

@@ -60,6 +60,7 @@ class DecodeConfig:
     eps: float = 1e-6
     seed: int = 208000
     description: str = ""
+    block_size: int = BLOCK_SIZE     # tokens per physical block (16 or 32)
 
     @property
     def group(self) -> int:
@@ -73,7 +74,7 @@ class DecodeConfig:
     def max_partitions(self) -> int:
         if self.partition_size == 0:
             return 1
-        return -(-self.mbs * BLOCK_SIZE // self.partition_size)
+        return -(-self.mbs * self.block_size // self.partition_size)
 
     def replace(self, **kw) -> "DecodeConfig":
         return dataclasses.replace(self, **kw)
@@ -133,7 +134,7 @@ def generate(cfg: DecodeConfig, *, seed: int | None = None) -> dict:
     gamma_q, gamma_k [D] f32 (fused config only); poison_block int; nb int.
     """
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
-    B, Hkv, D, BS = cfg.B, cfg.Hkv, cfg.D, BLOCK_SIZE
+    B, Hkv, D, BS = cfg.B, cfg.Hkv, cfg.D, cfg.block_size
 
     lens = rng.integers(cfg.len_lo, cfg.len_hi, size=B, endpoint=True).astype(np.int64)
     if cfg.prefix_tokens:
@@ -231,6 +232,6 @@ def kv_bytes(cfg: DecodeConfig, context_lens, window: int = 0) -> int:
     elem = 1 if cfg.kv_dtype == "e4m3" else 2
     b = tokens * cfg.Hkv * cfg.D * 2 * elem
     if cfg.kv_dtype == "e4m3":
-        tiles = int(np.sum(-(-lens // BLOCK_SIZE)))
+        tiles = int(np.sum(-(-lens // cfg.block_size)))
         b += tiles * cfg.Hkv * 2 * 4
     return b

@@ -130,6 +130,7 @@ def _append_args(**kw):
     (dict(k_pool=MIS), -1),
     (dict(D=32), -2),
     (dict(BS=8), -2),
+    (dict(BS=32), 0),
     (dict(gamma_k=A), -1),
     (dict(gamma_k=A, gamma_q=A, q=A, Hq=8, context_lens=A), 0),
     (dict(gamma_k=A, gamma_q=A, q=A, Hq=7, context_lens=A), -1),
@@ -186,6 +187,9 @@ def _step_args(**kw):
     (dict(partition_size=0, max_partitions=16, window=-1), -1),
     (dict(window=100), -2),
     (dict(n_query=0), -1),
+    (dict(BS=32), -2),
+    (dict(BS=32, partition_size=0, max_partitions=16), 0),
+    (dict(BS=48, partition_size=0, max_partitions=16), -2),
     (dict(n_query=2), -2),
     (dict(partition_size=0, max_partitions=16, n_query=4), 0),
     (dict(partition_size=0, max_partitions=16, n_query=3), -2),
@@ -230,7 +234,8 @@ def test_step_validation_codes(lib, kw, code):
     (dict(k_pool=MIS), -1),
     (dict(dst=A + 2), -1),
     (dict(D=96), -2),
-    (dict(BS=32), -2),
+    (dict(BS=32), 0),
+    (dict(BS=8), -2),
     (dict(kv_dtype=2), -1),
     (dict(kv_dtype=1), -1),
     (dict(kv_dtype=1, k_scale=A, v_scale=A), 0),
@@ -253,7 +258,8 @@ def test_copy_validation_codes(lib, kw, code):
     (dict(v_scale=A + 2), -1),
     (dict(slot_mapping=A + 4), -1),
     (dict(D=32), -2),
-    (dict(BS=32), -2),
+    (dict(BS=32), 0),
+    (dict(BS=64), -2),
     (dict(NB=0), -1),
 ])
 def test_append_e4m3_validation_codes(lib, kw, code):
