@@ -44,8 +44,8 @@
  * a failed check returns PKV_EINVAL or PKV_EUNSUPPORTED and enqueues
  * nothing.  A failed launch returns PKV_ELAUNCH.  Device-resident data is
  * the caller's contract and is NOT checked: block ids < NB for the first
- * ceil(L/16) table entries, 0 <= context_lens[b] <= MBS*16, distinct slots
- * < NB*16.  The result never depends on pool bytes outside a sequence's
+ * ceil(L/BS) table entries, 0 <= context_lens[b] <= MBS*BS, distinct slots
+ * < NB*BS.  The result never depends on pool bytes outside a sequence's
  * first context_lens[b] rows (they may hold NaN).
  */
 #ifndef PAGEDKV_H
