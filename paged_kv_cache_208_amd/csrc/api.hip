@@ -121,6 +121,7 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
   a.part_sum = part_sum;
   a.window = window;
   a.bs_tiles = BS / pkv::kBlockSize;
+  a.bs_shift = a.bs_tiles == 2 ? 1 : 0;
   a.nq = n_query;
   a.group = Hq / Hkv;
   a.Hq = Hq;

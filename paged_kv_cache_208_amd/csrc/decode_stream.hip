@@ -94,13 +94,13 @@ struct Totals {
 
 // L0: this lane's length in the first chunk of 64 sequences, read once by
 // the caller and used by both scans.
-__device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B, int L0) {
+__device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B, int L0, int W) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t tot = 0;
   int mx = 0;
   for (int c = 0; c < B; c += kWave) {
     const int b = c + lane;
-    const int T = seg_tiles(c == 0 ? L0 : b < B ? a.context_lens[b] : 0, a.window);
+    const int T = seg_tiles(c == 0 ? L0 : b < B ? a.context_lens[b] : 0, W);
     const int64_t incl = wave_scan(int64_t(T));
     tot += readlane64(incl, kWave - 1);
     mx = max(mx, T);
@@ -111,14 +111,14 @@ __device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B, int L0
 }
 
 // Cursor of flattened tile t (t < total).
-__device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, int L0) {
+__device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, int L0, int W) {
   const int lane = threadIdx.x & (kWave - 1);
   Cursor c{};
   int64_t carry = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
     const int L = c0 == 0 ? L0 : b < B ? a.context_lens[b] : 0;
-    const int64_t w = int64_t(a.Hkv) * seg_tiles(L, a.window);
+    const int64_t w = int64_t(a.Hkv) * seg_tiles(L, W);
     const int64_t hi = carry + wave_scan(w);
     const int64_t lo = hi - w;
     const uint64_t here = __builtin_amdgcn_ballot_w64(b < B && lo <= t && t < hi);
@@ -126,8 +126,8 @@ __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, 
       const int src = __builtin_ctzll(here);
       c.b = c0 + src;
       c.L = __builtin_amdgcn_readlane(L, src);
-      c.T = seg_tiles(c.L, a.window);
-      c.f = first_tile(c.L, a.window);
+      c.T = seg_tiles(c.L, W);
+      c.f = first_tile(c.L, W);
       const int64_t off = t - readlane64(lo, src);
       c.kvh = int(off / c.T);
       c.n = int(off % c.T);
@@ -140,7 +140,7 @@ __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, 
 }
 
 // Next tile in the flattened order (skips sequences with no tokens).
-__device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B) {
+__device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B, int W) {
   if (++c.n < c.T) return;
   c.n = 0;
   c.S += c.T;
@@ -150,8 +150,8 @@ __device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B) {
     if (++c.b >= B) return;
     c.L = load_uniform(a.context_lens + c.b);
   } while (c.L == 0);
-  c.T = seg_tiles(c.L, a.window);
-  c.f = first_tile(c.L, a.window);
+  c.T = seg_tiles(c.L, W);
+  c.f = first_tile(c.L, W);
 }
 
 // What the loop needs to know about a tile besides its data.
@@ -166,15 +166,16 @@ struct Meta {
   bool last;   // last tile of the wave's piece of the segment
 };
 
+// W: window (0 = full); bst / shift: 16-token tiles per block and log2.
 __device__ __forceinline__ Meta meta_of(const Cursor& c, const DecodeArgs& a, int64_t t, int64_t t0,
-                                        int64_t t1) {
+                                        int64_t t1, int W, int bst, int shift) {
   Meta m;
   // a scalar load; its result is first needed one loop step later
-  m.id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + (c.f + c.n) / a.bs_tiles);
-  m.half = (c.f + c.n) % a.bs_tiles;
+  m.id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + ((c.f + c.n) >> shift));
+  m.half = (c.f + c.n) & (bst - 1);
   m.slot = 0;
   m.f = c.f;
-  m.lo = c.n == 0 ? window_start(c.L, a.window) - 16 * c.f : 0;
+  m.lo = c.n == 0 ? window_start(c.L, W) - 16 * c.f : 0;
   m.b = c.b;
   m.kvh = c.kvh;
   m.n = c.n;
@@ -186,9 +187,17 @@ __device__ __forceinline__ Meta meta_of(const Cursor& c, const DecodeArgs& a, in
   return m;
 }
 
-template <int D, int C, bool FP8, int MODE>
+// EXT: the window, several new tokens per sequence or 32-token blocks are in
+// use; without it they are compile-time constants (full attention, one
+// token, 16-token blocks) and the common kernel carries none of their code.
+template <int D, int C, bool FP8, int MODE, bool EXT>
 struct StreamKernel {
   using Geo = MfmaGeo<D, FP8>;
+  static __device__ __forceinline__ int W(const DecodeArgs& a) { return EXT ? a.window : 0; }
+  static __device__ __forceinline__ int NQ(const DecodeArgs& a) { return EXT ? a.nq : 1; }
+  static __device__ __forceinline__ int GRP(const DecodeArgs& a) { return EXT ? a.group : C; }
+  static __device__ __forceinline__ int BST(const DecodeArgs& a) { return EXT ? a.bs_tiles : 1; }
+  static __device__ __forceinline__ int BSS(const DecodeArgs& a) { return EXT ? a.bs_shift : 0; }
   static constexpr bool APPEND = (MODE & kModeAppend) != 0;
   static constexpr bool QKNORM = (MODE & kModeQkNorm) != 0;
   // tiles in the load pipeline of a wave
@@ -198,7 +207,7 @@ struct StreamKernel {
   // token col / g of q head kvh * g + col % g (g = Hq / Hkv; one new token
   // per sequence unless nq > 1).  Row of q and of out [B][nq][Hq][D]:
   static __device__ __forceinline__ size_t qrow(const DecodeArgs& a, int b, int kvh, int col) {
-    return (size_t(b) * a.nq + col / a.group) * a.Hq + kvh * a.group + col % a.group;
+    return (size_t(b) * NQ(a) + col / GRP(a)) * a.Hq + kvh * GRP(a) + col % GRP(a);
   }
 
   // q of head slot n16 of the segment's group, laid out as the B operand of
@@ -208,9 +217,9 @@ struct StreamKernel {
   // first tile is computed, once the loads have landed.
   static __device__ __forceinline__ void load_q(half8_t* qop, const DecodeArgs& a, int b, int kvh,
                                                 int g, int n16) {
-    const size_t base = size_t(b) * a.nq * a.Hq;
+    const size_t base = size_t(b) * NQ(a) * a.Hq;
     const _Float16* qs = static_cast<const _Float16*>(a.q) + base * D;
-    const int span = a.nq * a.Hq * D;  // the sequence's q rows
+    const int span = NQ(a) * a.Hq * D;  // the sequence's q rows
     const __amdgpu_buffer_rsrc_t r = make_rsrc(qs, span * int(sizeof(_Float16)));
     const int row = n16 < C ? int(qrow(a, b, kvh, n16) - base) * D : span;
 #pragma unroll
@@ -232,12 +241,12 @@ struct StreamKernel {
                                                      const float* s_gk) {
     using VW = typename Words<Geo::kVWords>::T;
     while (c.S < t1) {
-      for (int i = 0; i < a.nq; ++i) {
-        const int p = c.L - a.nq + i;             // position of new token i
+      for (int i = 0; i < NQ(a); ++i) {
+        const int p = c.L - NQ(a) + i;            // position of new token i
         const int64_t tile = c.S + (p / 16 - c.f);
         if (p < 0 || tile < t0 || tile >= t1) continue;
-        const int id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + p / 16 / a.bs_tiles);
-        const size_t row = (size_t(c.b) * a.nq + i) * a.Hkv + c.kvh;
+        const int id = load_uniform(a.block_tables + size_t(c.b) * a.MBS + ((p / 16) >> BSS(a)));
+        const size_t row = (size_t(c.b) * NQ(a) + i) * a.Hkv + c.kvh;
         const _Float16* kn = static_cast<const _Float16*>(a.k_new) + row * D;
         const _Float16* vn = static_cast<const _Float16*>(a.v_new) + row * D;
         half8_t kc[Geo::kKLoads];
@@ -250,8 +259,8 @@ struct StreamKernel {
           norm_rope_chunks<D>(kc, s_gk, a.eps, s_cos, s_sin, g);
         }
         const int r_new = p % 16;
-        const size_t base = ((size_t(id) * a.Hkv + c.kvh) * a.bs_tiles + (p / 16) % a.bs_tiles) *
-                            Geo::kTile;
+        const size_t base =
+            ((size_t(id) * a.Hkv + c.kvh) * BST(a) + ((p / 16) & (BST(a) - 1))) * Geo::kTile;
         uint8_t* kt = const_cast<uint8_t*>(a.k_pool) + base;
         uint8_t* vt = const_cast<uint8_t*>(a.v_pool) + base;
         if (n16 == r_new)
@@ -262,7 +271,7 @@ struct StreamKernel {
       }
       // on to the next segment
       c.n = c.T - 1;
-      advance(c, a, B);
+      advance(c, a, B, W(a));
       if (c.b >= B) break;
     }
   }
@@ -274,7 +283,7 @@ struct StreamKernel {
   static __device__ __forceinline__ void issue(MTile<D, FP8>& t, const DecodeArgs& a, const Meta& m,
                                                bool live, int k_off, int v_off) {
     const size_t base =
-        live ? ((size_t(m.id) * a.Hkv + m.kvh) * a.bs_tiles + m.half) * Geo::kTile : 0;
+        live ? ((size_t(m.id) * a.Hkv + m.kvh) * BST(a) + m.half) * Geo::kTile : 0;
     load_mtile_at<D, FP8>(t, a, base, live ? min(16, m.L - 16 * (m.f + m.n)) : 0, k_off, v_off);
     t.lo = live ? m.lo : 0;
   }
@@ -493,10 +502,11 @@ struct StreamKernel {
   }
 };
 
-template <int D, int C, bool FP8, int MODE>
+template <int D, int C, bool FP8, int MODE, bool EXT>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<FP8>(), 8)))
 void decode_stream_kernel(DecodeArgs a, int B, int workers) {
-  using K = StreamKernel<D, C, FP8, MODE>;
+  using K = StreamKernel<D, C, FP8, MODE, EXT>;
+  const int win = K::W(a);
   using Geo = MfmaGeo<D, FP8>;
   static_assert(C <= 16, "head slots of one 16-wide product");
   const int lane = threadIdx.x;
@@ -505,7 +515,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   const int n16 = lane % 16;
   const int k_off = n16 * Geo::kRow + g * 16;
   const int v_off = (4 * g) * Geo::kRow + n16 * Geo::kVBytes;
-  const int jcol = n16 < C ? n16 / a.group : 0;  // new query token of this lane's column
+  const int jcol = n16 < C ? n16 / K::GRP(a) : 0;  // new query token of this lane's column
 
   __shared__ float s_w[2 * C * kMaxStepPartitions];  // combine weights
   __shared__ float s_fin[K::kStage];                  // the range's last piece
@@ -520,7 +530,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   __shared__ float s_gk[K::QKNORM ? D : 1];
 
   const int L0 = lane < B ? a.context_lens[lane] : 0;
-  const Totals tot = total_tiles(a, B, L0);
+  const Totals tot = total_tiles(a, B, L0, win);
   const int64_t W = tot.tiles;
   // equal shares, but long enough that no sequence's segment is cut into more
   // than max_partitions pieces: T tiles span at most (T-1)/tpw + 2 ranges
@@ -530,7 +540,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   const int64_t t1 = min(W, t0 + tpw);
 
   if (t0 < t1) {
-    Cursor cur = locate(a, B, t0, L0);
+    Cursor cur = locate(a, B, t0, L0, win);
     int rope_b[2] = {-1, -1};  // sequence whose angles are in each table
     int ord = 0;                // segments entered so far; parity picks the table
     if constexpr (K::QKNORM) {
@@ -579,7 +589,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       }
       last_slot = m.slot;
     };
-    mt[0] = meta_of(cur, a, t0, t0, t1);
+    mt[0] = meta_of(cur, a, t0, t0, t1, win, K::BST(a), K::BSS(a));
     mt[0].first = true;  // the range starts with a piece of a segment
     take(mt[0], qbuf[0]);
     K::issue(tl[0], a, mt[0], true, k_off, v_off);
@@ -587,8 +597,8 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
     for (int k = 1; k < NB; ++k) {
       const bool live = t0 + k < t1;
       if (live) {
-        advance(cur, a, B);
-        Meta m = meta_of(cur, a, t0 + k, t0, t1);
+        advance(cur, a, B, win);
+        Meta m = meta_of(cur, a, t0 + k, t0, t1, win, K::BST(a), K::BSS(a));
         if (k < NB - 1) {
           mt[k] = m;
           take(mt[k], qbuf[k]);
@@ -618,8 +628,8 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       }
       K::issue(y, a, my, live, k_off, v_off);
       if (t + NB < t1) {
-        advance(cur, a, B);
-        ahead = meta_of(cur, a, t + NB, t0, t1);
+        advance(cur, a, B, win);
+        ahead = meta_of(cur, a, t + NB, t0, t1, win, K::BST(a), K::BSS(a));
       }
       issue_fence();  // Y's loads stay ahead of the waits below
       if (mx.first) {
@@ -632,7 +642,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       issue_fence();
       // causal limit of this lane's column: new token j sees positions up to
       // L - nq + j (rows of tile f + n at or past the limit are masked)
-      const int col_hi = mx.L - a.nq + 1 + jcol - 16 * (mx.f + mx.n);
+      const int col_hi = EXT ? mx.L - K::NQ(a) + 1 + jcol - 16 * (mx.f + mx.n) : 16;
       mfma_tile<D, FP8>(st, x, qop, a.scale_log2, g, col_hi);
       if (t + 1 >= t1) {
         mfin = mx;
@@ -697,8 +707,8 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   // sequences with no tokens: zero output rows, one wave each
   for (int b = worker; b < B; b += workers)
     if (load_uniform(a.context_lens + b) == 0)
-      for (int i = lane; i < a.nq * a.Hq * D; i += kWave)
-        static_cast<_Float16*>(a.out)[size_t(b) * a.nq * a.Hq * D + i] = (_Float16)0.0f;
+      for (int i = lane; i < K::NQ(a) * a.Hq * D; i += kWave)
+        static_cast<_Float16*>(a.out)[size_t(b) * K::NQ(a) * a.Hq * D + i] = (_Float16)0.0f;
 }
 
 // Compute units of the current device (queried once per device).
@@ -719,8 +729,13 @@ int device_cus() {
 template <int D, int C, bool FP8, int MODE>
 hipError_t launch_stream(const DecodeArgs& a, int B, hipStream_t stream) {
   const int workers = device_cus() * 4 * stream_waves_per_eu<FP8>();
-  hipLaunchKernelGGL((decode_stream_kernel<D, C, FP8, MODE>), dim3(workers), dim3(kWave), 0, stream,
-                     a, B, workers);
+  const bool ext = a.window > 0 || a.nq > 1 || a.bs_tiles > 1;
+  if (ext)
+    hipLaunchKernelGGL((decode_stream_kernel<D, C, FP8, MODE, true>), dim3(workers), dim3(kWave), 0,
+                       stream, a, B, workers);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<D, C, FP8, MODE, false>), dim3(workers), dim3(kWave),
+                       0, stream, a, B, workers);
   return hipGetLastError();
 }
 

@@ -191,7 +191,7 @@ __device__ __forceinline__ void load_mtile_at(MTile<D, FP8>& t, const DecodeArgs
   t.ks = t.vs = 1.0f;
   if constexpr (FP8) {
     if (rows > 0) {
-      const size_t s = base / Geo::kTile / a.bs_tiles;  // == block id * Hkv + kv head
+      const size_t s = (base / Geo::kTile) >> a.bs_shift;  // == block id * Hkv + kv head
       t.ks = load_uniform_f32(a.k_scale + s);
       t.vs = load_uniform_f32(a.v_scale + s);
     }

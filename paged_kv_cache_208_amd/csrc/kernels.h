@@ -33,6 +33,7 @@ struct DecodeArgs {
   int nq;                     // new query tokens per sequence (balanced step; 1 otherwise)
   int group;                  // Hq / Hkv
   int bs_tiles;               // 16-token tiles per block: 1, or 2 for 32-token blocks
+  int bs_shift;               // log2(bs_tiles)
 };
 
 // What a decode launch does besides attending (bit flags).
