@@ -7,10 +7,12 @@ into paged_kv_cache_208_amd/libpagedkv.so.  hipcc cross-compiles for gfx950,
 so this runs on machines without a GPU.
 """
 
+import concurrent.futures
 import glob
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -34,19 +36,39 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "validate.cpp")]
 
 
-def build(out=LIB, extra=(), verbose=False):
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *DEVICE_FLAGS, *extra, "-o", out + ".tmp", *sources()]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag: harmless
     err = "\n".join(ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+    return res.returncode, err
+
+
+def build(out=LIB, extra=(), verbose=False, jobs=None):
+    """Compile each source to an object in parallel, then link the library."""
+    common = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+              "-Wno-unused-result", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+              *DEVICE_FLAGS, *extra]
+    srcs = sources()
+    jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    with tempfile.TemporaryDirectory(prefix="pagedkv_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
+        cmds = [common + ["-c", "-o", o, s] for s, o in zip(srcs, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+            results = list(pool.map(_run, cmds))
+        for (rc, err), s in zip(results, srcs):
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed on {os.path.basename(s)} ({rc}):\n{err}")
+            if err.strip() and verbose:
+                print(err, file=sys.stderr)
+        link = [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", "-o", out + ".tmp", *objs]
+        if verbose:
+            print(" ".join(link), flush=True)
+        rc, err = _run(link)
+        if rc != 0:
+            raise RuntimeError(f"hipcc link failed ({rc}):\n{err}")
     os.replace(out + ".tmp", out)
     return out
 

@@ -240,12 +240,18 @@ __device__ __forceinline__ half4_t v_operand(const MTile<D, FP8>& t, int i) {
     const u32x2 r = {lo, hi};
     return __builtin_bit_cast(half4_t, r);
   } else {
-    const int wi = i / 4, sh = 8 * (i % 4);
-    const uint32_t b0 = (word<Geo::kVWords>(t.v[0], wi) >> sh) & 0xFFu;
-    const uint32_t b1 = (word<Geo::kVWords>(t.v[1], wi) >> sh) & 0xFFu;
-    const uint32_t b2 = (word<Geo::kVWords>(t.v[2], wi) >> sh) & 0xFFu;
-    const uint32_t b3 = (word<Geo::kVWords>(t.v[3], wi) >> sh) & 0xFFu;
-    const uint32_t w = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    // byte i % 4 of word i / 4 of rows 0..3 gathered into one word by byte
+    // permutes: rows (0, 1) and (2, 3) pair up the bytes of i and its
+    // neighbour i ^ 1, and a third permute picks i's half of each pair
+    const int wi = i / 4, k = i % 4 & ~1;
+    const uint32_t x0 = word<Geo::kVWords>(t.v[0], wi), x1 = word<Geo::kVWords>(t.v[1], wi);
+    const uint32_t x2 = word<Geo::kVWords>(t.v[2], wi), x3 = word<Geo::kVWords>(t.v[3], wi);
+    // perm(hi, lo, sel): selector byte s takes byte s of {hi:lo} (lo = bytes 0..3)
+    const uint32_t sel = uint32_t(k) | uint32_t(k + 4) << 8 | uint32_t(k + 1) << 16 |
+                         uint32_t(k + 5) << 24;
+    const uint32_t p01 = __builtin_amdgcn_perm(x1, x0, sel);
+    const uint32_t p23 = __builtin_amdgcn_perm(x3, x2, sel);
+    const uint32_t w = __builtin_amdgcn_perm(p23, p01, i % 2 ? 0x07060302u : 0x05040100u);
     const half2_t a = e4m3x2_to_half2<false>(w), c = e4m3x2_to_half2<true>(w);
     return half4_t{a.x, a.y, c.x, c.y};
   }

@@ -57,10 +57,10 @@ __device__ __forceinline__ half2_t as_half2(uint32_t w) { return __builtin_bit_c
 
 // Two E4M3 (OCP FN) codes in the low (hi == false) or high half of `w` to
 // two fp16 values, exactly (every finite E4M3 value is an fp16 value).
+// One gfx950 conversion (scale 1.0, so no rounding happens).
 template <bool HI>
 __device__ __forceinline__ half2_t e4m3x2_to_half2(uint32_t w) {
-  float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-  return half2_t{(_Float16)f.x, (_Float16)f.y};
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
 }
 
 template <bool HI>
