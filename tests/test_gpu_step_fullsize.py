@@ -1,0 +1,158 @@
+"""GPU parity of the one-launch balanced step at the full sizes of the
+model-shaped workloads, in the launch configuration bench.py times
+(partition_size 0, a 16-deep workspace): 1024 or 2048 waves, ranges of
+dozens to hundreds of tiles, most sequences cut into several pieces that
+the kernel combines.
+
+Each case checks the output against the fp64 oracle (all sequences, or a
+seeded sample where the oracle would take long), the appended rows bitwise,
+that a second call gives bitwise the same output, and that every arrival
+counter is back at zero.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import append_ref, attn_ref, fused_append_ref, mq_attn_ref
+from paged_kv_cache_208_amd import _lib
+
+from helpers import TOL_E4M3, TOL_F16, batch, dev, max_abs, sample_seqs, to_device
+
+pytestmark = pytest.mark.gpu
+
+SPLITS = 16  # bench.py's default workspace depth
+
+
+def _u16(x):
+    return np.ascontiguousarray(x).view(np.uint16)
+
+
+def _run(cfg, g, P, *, append=True, qknorm=False, window=0, q=None, k_new=None, v_new=None,
+         reps=2):
+    q = g["q"] if q is None else q
+    shape = tuple(q.shape)
+    nq = shape[1] if q.dim() == 4 else 1
+    ws = _lib.alloc_step_workspace(cfg.B, cfg.Hq * nq, cfg.Hkv, cfg.D, P)
+    kw = {}
+    if append:
+        kw.update(k_new=g["k_new"] if k_new is None else k_new,
+                  v_new=g["v_new"] if v_new is None else v_new)
+    if qknorm:
+        kw.update(gamma_q=g["gamma_q"], gamma_k=g["gamma_k"], eps=cfg.eps, rope_theta=cfg.theta)
+    outs = []
+    q0 = q.clone() if qknorm else None
+    for r in range(reps):
+        if r and qknorm:       # the step rewrote q in place: start again from q
+            q.copy_(q0)
+        out = torch.full(shape, float("nan"), dtype=torch.float16, device="cuda")
+        _lib.paged_decode_step(out, q, g["k_pool"], g["v_pool"], g["block_tables"],
+                               g["context_lens"], cfg.scale, k_scale=g.get("k_scale"),
+                               v_scale=g.get("v_scale"), partition_size=0, window=window,
+                               workspace=ws, **kw)
+        torch.cuda.synchronize()
+        outs.append(out)
+        assert torch.count_nonzero(ws[3]).item() == 0, "counters not back at zero"
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    return outs[0]
+
+
+@pytest.mark.parametrize("P", [3, SPLITS, 64])
+def test_fullsize_llama_shape_append(P):
+    """B=32, 32/8 heads, d=128, contexts 512..4096 with the step's append
+    (P = 3: ranges long enough that no sequence is cut into more than three
+    pieces)."""
+    cfg, d = batch("c2")
+    g = to_device(d)
+    out = _run(cfg, g, P)
+    kp, vp = append_ref(d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], d["slot_mapping"])
+    assert np.array_equal(_u16(g["k_pool"].cpu().numpy()), _u16(kp))
+    assert np.array_equal(_u16(g["v_pool"].cpu().numpy()), _u16(vp))
+    ref = attn_ref(d["q"], kp, vp, d["block_tables"], d["context_lens"], cfg.scale)
+    assert max_abs(out, ref) <= TOL_F16
+
+
+def test_fullsize_e4m3_70b_shape():
+    """B=64, 64/8 heads, E4M3 KV, contexts 3600..4400 (two waves per SIMD)."""
+    cfg, d = batch("c5")
+    g = to_device(d)
+    out = _run(cfg, g, SPLITS, append=False)
+    seqs = sample_seqs(cfg.B, 6, seed=5)
+    ref = attn_ref(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                   cfg.scale, k_scale=d["k_scale"], v_scale=d["v_scale"], seqs=seqs)
+    assert max_abs(out[seqs], ref[seqs]) <= TOL_E4M3
+
+
+def test_fullsize_shared_prefix_many_sequences():
+    """B=128 with a 1024-token prefix shared by every table."""
+    cfg, d = batch("c3")
+    g = to_device(d)
+    out = _run(cfg, g, SPLITS)
+    kp, vp = append_ref(d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], d["slot_mapping"])
+    assert np.array_equal(_u16(g["k_pool"].cpu().numpy()), _u16(kp))
+    seqs = sample_seqs(cfg.B, 10, seed=3)
+    ref = attn_ref(d["q"], kp, vp, d["block_tables"], d["context_lens"], cfg.scale, seqs=seqs)
+    assert max_abs(out[seqs], ref[seqs]) <= TOL_F16
+
+
+def test_fullsize_qknorm_rope():
+    """Qwen3-shaped QK-norm + RoPE + append (B=64, contexts up to 4096): q'
+    is written back once per (sequence, kv head) by the wave that combines."""
+    cfg, d = batch("c4", B=64, len_hi=4096, mbs=256)
+    g = to_device(d)
+    out = _run(cfg, g, SPLITS, qknorm=True, reps=2)
+    q2, kp, vp, _, _ = fused_append_ref(d["q"], d["k_new"], d["v_new"], d["k_pool"],
+                                        d["v_pool"], d["slot_mapping"], d["context_lens"],
+                                        d["gamma_q"], d["gamma_k"], cfg.eps, cfg.theta)
+    gq = g["q"].cpu().numpy()
+    ulp = np.spacing(np.maximum(np.abs(q2), np.abs(gq)).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(gq.astype(np.float64) - q2.astype(np.float64)) <= ulp)
+    seqs = sample_seqs(cfg.B, 8, seed=4)
+    ref = attn_ref(q2, kp, vp, d["block_tables"], d["context_lens"], cfg.scale, seqs=seqs)
+    assert max_abs(out[seqs], ref[seqs]) <= TOL_F16
+
+
+def test_fullsize_sliding_window():
+    cfg, d = batch("c2")
+    win = 1000
+    g = to_device(d)
+    out = _run(cfg, g, SPLITS, window=win)
+    kp, vp = append_ref(d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], d["slot_mapping"])
+    ref = attn_ref(d["q"], kp, vp, d["block_tables"], d["context_lens"], cfg.scale, window=win)
+    assert max_abs(out, ref) <= TOL_F16
+
+
+def test_fullsize_multi_token():
+    """Two new tokens per sequence (causal), rows appended bitwise."""
+    cfg, d = batch("c2")
+    nq = 2
+    rng = np.random.default_rng(72)
+    B, Hq, Hkv, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.D
+    q = rng.standard_normal((B, nq, Hq, D)).astype(np.float16)
+    kn = rng.standard_normal((B, nq, Hkv, D)).astype(np.float16)
+    vn = rng.standard_normal((B, nq, Hkv, D)).astype(np.float16)
+    tab, lens = d["block_tables"], d["context_lens"]
+    slots = np.array([int(tab[b, p // 16]) * 16 + p % 16
+                      for b in range(B) for p in range(int(lens[b]) - nq, int(lens[b]))],
+                     dtype=np.int64)
+    g = to_device(d)
+    out = _run(cfg, g, SPLITS, q=dev(q), k_new=dev(kn), v_new=dev(vn))
+    kp, vp = append_ref(d["k_pool"], d["v_pool"], kn.reshape(B * nq, Hkv, D),
+                        vn.reshape(B * nq, Hkv, D), slots)
+    assert np.array_equal(_u16(g["k_pool"].cpu().numpy()), _u16(kp))
+    assert np.array_equal(_u16(g["v_pool"].cpu().numpy()), _u16(vp))
+    ref = mq_attn_ref(q, kp, vp, tab, lens, cfg.scale)
+    assert max_abs(out, ref) <= TOL_F16
+
+
+def test_fullsize_block32():
+    cfg, d = batch("c2", block_size=32, mbs=128)
+    g = to_device(d)
+    out = _run(cfg, g, SPLITS)
+    kp, vp = append_ref(d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], d["slot_mapping"],
+                        block_size=32)
+    assert np.array_equal(_u16(g["k_pool"].cpu().numpy()), _u16(kp))
+    ref = attn_ref(d["q"], kp, vp, d["block_tables"], d["context_lens"], cfg.scale,
+                   block_size=32)
+    assert max_abs(out, ref) <= TOL_F16
