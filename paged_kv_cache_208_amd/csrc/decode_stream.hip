@@ -7,11 +7,12 @@
 // Serving Platform", section 2: logical block n of a sequence is found
 // through its block table).  With W tiles in total and C waves (a fixed
 // number per CU), wave w reads the contiguous range [w*tpw, (w+1)*tpw),
-// tpw = ceil(W / C).  Every wave therefore moves the same number of bytes,
-// whatever the mix of context lengths, and streams straight across the
-// boundaries between (sequence, kv head) segments: the next tile's loads are
-// issued before the current tile is computed, whichever segment it belongs
-// to.
+// tpw = ceil(W / C) (with two waves per SIMD the first C/2 ranges are a
+// little longer; see Ranges).  Every wave therefore moves about the same
+// number of bytes, whatever the mix of context lengths, and streams straight
+// across the boundaries between (sequence, kv head) segments: the next
+// tile's loads are issued before the current tile is computed, whichever
+// segment it belongs to.
 //
 // A segment that lies inside one wave's range is finished by that wave (the
 // normalised output is written directly).  A segment shared by several
@@ -154,6 +155,43 @@ __device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B, i
   c.f = first_tile(c.L, W);
 }
 
+#ifndef PKV_STREAM_SKEW_FP8
+#define PKV_STREAM_SKEW_FP8 120
+#endif
+
+// The wave ranges: the first H = workers / 2 waves read ranges of ta tiles,
+// the others ranges of tb, back to back in the flattened order.  With two
+// waves per SIMD the first wave placed on a SIMD is served first when both
+// are ready to issue, and equal shares end far apart; the first half then
+// takes the larger share (skew ta : tb, in percent).  Every range is long
+// enough that no sequence is cut into more than P pieces: T tiles span at
+// most (T - 1) / r + 2 ranges of r >= rmin tiles.
+struct Ranges {
+  int64_t ta, tb, H;
+  __device__ __forceinline__ int64_t start(int64_t w) const {
+    return w <= H ? w * ta : H * ta + (w - H) * tb;
+  }
+  __device__ __forceinline__ int64_t of(int64_t t) const {  // range holding tile t
+    return t < H * ta ? t / ta : H + (t - H * ta) / tb;
+  }
+};
+
+template <bool FP8>
+__device__ __forceinline__ Ranges make_ranges(int64_t W, int Tmax, int workers, int P) {
+  const int64_t rmin = max(int64_t(1), int64_t(Tmax + P - 3) / (P - 2));
+  const int skew = FP8 ? PKV_STREAM_SKEW_FP8 : 100;
+  Ranges r;
+  r.H = workers / 2;
+  if (skew == 100) {
+    r.ta = r.tb = max((W + workers - 1) / workers, rmin);
+    return r;
+  }
+  // W * skew / (skew + 100) tiles for the first half
+  r.ta = max((W * skew / (skew + 100) + r.H - 1) / r.H, rmin);
+  r.tb = max((max(W - r.H * r.ta, int64_t(0)) + (workers - r.H) - 1) / (workers - r.H), rmin);
+  return r;
+}
+
 // What the loop needs to know about a tile besides its data.
 struct Meta {
   int b, kvh, n, L, T, f;
@@ -288,9 +326,9 @@ struct StreamKernel {
     t.lo = live ? m.lo : 0;
   }
 
-  // Pieces the wave ranges cut segment m into (tpw tiles per range).
-  static __device__ __forceinline__ int pieces_of(const Meta& m, int64_t tpw) {
-    return int((m.S + m.T - 1) / tpw - m.S / tpw + 1);
+  // Pieces the wave ranges cut segment m into.
+  static __device__ __forceinline__ int pieces_of(const Meta& m, const Ranges& rg) {
+    return int(rg.of(m.S + m.T - 1) - rg.of(m.S) + 1);
   }
 
   // Output rows of a segment that lies inside one wave's range: o / l.
@@ -534,10 +572,9 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   const int64_t W = tot.tiles;
   // equal shares, but long enough that no sequence's segment is cut into more
   // than max_partitions pieces: T tiles span at most (T-1)/tpw + 2 ranges
-  const int64_t tpw = max((W + workers - 1) / workers,
-                          int64_t(tot.max_tiles + a.max_partitions - 3) / (a.max_partitions - 2));
-  const int64_t t0 = int64_t(worker) * tpw;
-  const int64_t t1 = min(W, t0 + tpw);
+  const Ranges rg = make_ranges<FP8>(W, tot.max_tiles, workers, a.max_partitions);
+  const int64_t t0 = min(rg.start(worker), W);
+  const int64_t t1 = min(W, rg.start(worker + 1));
 
   if (t0 < t1) {
     Cursor cur = locate(a, B, t0, L0, win);
@@ -649,7 +686,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
         return;
       }
       if (mx.last) {
-        const int pieces = K::pieces_of(mx, tpw);
+        const int pieces = K::pieces_of(mx, rg);
         const int seg = mx.b * a.Hkv + mx.kvh;
         const float l = group4_sum(st.l);
         if (pieces == 1) {
@@ -661,7 +698,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
           pend = true;
           pseg = seg;
           ppieces = pieces;
-          pj = int(worker - mx.S / tpw);
+          pj = int(worker - rg.of(mx.S));
         }
         K::reset(st);
       }
@@ -678,7 +715,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
 
     // the range's last piece
     const Meta& mf = mfin;
-    const int fpieces = K::pieces_of(mf, tpw);
+    const int fpieces = K::pieces_of(mf, rg);
     const int fseg = mf.b * a.Hkv + mf.kvh;
     const float l = group4_sum(st.l);
     if (fpieces == 1) {
@@ -686,7 +723,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       if constexpr (K::QKNORM) K::write_q(a, fseg, qop, g, n16);
     } else {
       K::stage_partial(st, l, g, n16, s_fin);
-      K::write_partial(a, size_t(fseg) * C, int(worker - mf.S / tpw), s_fin);
+      K::write_partial(a, size_t(fseg) * C, int(worker - rg.of(mf.S)), s_fin);
     }
     if (pend) K::write_partial(a, size_t(pseg) * C, pj, s_pend);
     if (pend || fpieces > 1) {
