@@ -83,6 +83,13 @@ def parse():
                         "per sequence into E4M3 blocks (use an E4M3 config, c5)")
     p.add_argument("--copy-pairs", type=int, default=2048,
                    help="block pairs per copy-blocks launch")
+    p.add_argument("--read-ceiling-mib", type=int, default=1024,
+                   help="after timing, read a buffer of this many MiB with the library's "
+                        "streaming-read kernel and report the step's rate against it "
+                        "(0 = skip)")
+    p.add_argument("--paging-overhead", action="store_true",
+                   help="also time the same steps with every sequence's blocks made "
+                        "physically consecutive, and report the cost of paging itself")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after timing, run plain device copies of this many MiB (a known-size "
                         "kernel that profiler byte counters can be scaled against)")
@@ -425,6 +432,49 @@ def main():
     dec_ms = [ev["d0"][i].elapsed_time(ev["d1"][i]) for i in range(K)]
     dec_avg = float(np.mean(dec_ms))
 
+    def back_to_back():
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for i in range(K):
+            step(i)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / K
+
+    paging = None
+    if args.paging_overhead:
+        # the same batch with each sequence's blocks made consecutive
+        del copies[:]
+        torch.cuda.synchronize()
+        d2 = synth.contiguous_layout(cfg, d)
+        base2 = {k: up(v) for k, v in d2.items() if isinstance(v, np.ndarray)}
+        copies.extend([base2] + [{k: v.clone() for k, v in base2.items()} for _ in range(R - 1)])
+        ms_contig = back_to_back()
+        paging = {"ms_per_step_contiguous": round(ms_contig, 5),
+                  "overhead_pct": round(100.0 * (ms / ms_contig - 1.0), 2)}
+        del copies[:], base2, d2
+        torch.cuda.synchronize()
+
+    ceiling = None
+    if args.read_ceiling_mib:
+        nbytes = args.read_ceiling_mib << 20
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            _lib.pkv_stream_read(buf, sink, stream=stream)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record(stream)
+        for _ in range(10):
+            _lib.pkv_stream_read(buf, sink, stream=stream)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        ceiling = nbytes / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+        del buf, sink
+
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -476,6 +526,9 @@ def main():
         "steps_per_s": round(1e3 / ms, 1),
         "tokens_per_s": round(cfg.B * nq * 1e3 / ms, 1),
         "pct_hbm_peak": round(100 * value / HBM_GBPS, 2),
+        "read_ceiling_gbps": None if ceiling is None else round(ceiling, 1),
+        "pct_of_read_ceiling": None if ceiling is None else round(100 * value / ceiling, 2),
+        "paging": paging,
         "kv_bytes_per_step": kv,
         "decode_kernel_us": round(dec_avg * 1e3, 3),
         "decode_kernel_us_p10_p50_p90": [round(float(np.percentile(dec_ms, q)) * 1e3, 2)

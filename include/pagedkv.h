@@ -293,6 +293,21 @@ int pkv_validate_copy(const void* k_pool, const void* v_pool, const float* k_sca
                       const float* v_scale, const int32_t* src, const int32_t* dst, int n,
                       int Hkv, int D, int BS, int64_t NB, int kv_dtype);
 
+/*
+ * pkv_stream_read - read a device buffer once, front to back, as fast as the
+ * GPU allows.  A measurement yardstick, not part of the attention path: the
+ * bench times it to report the step's KV rate as a fraction of the read rate
+ * this GPU actually reaches (the spec sheet's 8 TB/s is not reached by any
+ * kernel).
+ *
+ * buf: device memory, 16-byte aligned, bytes a multiple of 16 (0 is a
+ * no-op).  sink: one uint32 of device memory; it is written only if the XOR
+ * of all 32-bit words read equals 0x9E3779B9 (so that the reads cannot be
+ * dropped), and then receives that value.  Returns PKV_EINVAL for a null
+ * pointer, misalignment or a bad size, PKV_ELAUNCH if the launch fails.
+ */
+int pkv_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

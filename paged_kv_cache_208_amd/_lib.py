@@ -40,6 +40,7 @@ _SIGNATURES = {
     "paged_kv_copy_blocks": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I, _P]),
     "paged_kv_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P]),
     "paged_attn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "pkv_stream_read": (_I, [_P, _I64, _P, _P]),
     "pkv_strerror": (ctypes.c_char_p, [_I]),
     "pkv_validate_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
                                  _F, _F]),
@@ -191,6 +192,17 @@ def paged_kv_copy_blocks(k_pool, v_pool, src, dst, *, k_scale=None, v_scale=None
                                     _ptr(src), _ptr(dst), src.shape[0], Hkv, D, BS, NB, kv,
                                     _stream(stream))
     _raise("paged_kv_copy_blocks", st)
+
+
+def pkv_stream_read(buf, sink, *, stream=None):
+    """Read the whole of `buf` (a contiguous GPU tensor, 16-byte multiple)
+    once: the read-ceiling yardstick.  `sink` is a 1-element int32 tensor."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _check(sink, "sink", torch.int32, 1)
+    st = lib().pkv_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                               _stream(stream))
+    _raise("pkv_stream_read", st)
 
 
 def max_partitions_for(max_blocks_per_seq: int, partition_size: int) -> int:

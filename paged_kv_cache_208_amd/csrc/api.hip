@@ -2,6 +2,7 @@
 // include/pagedkv.h): validate on the host, then enqueue the kernels.
 #include "pagedkv.h"
 #include "kernels.h"
+#include "read_probe.h"
 #include "device.h"
 #include "shape_limits.h"
 
@@ -170,4 +171,18 @@ extern "C" int paged_kv_append_e4m3(const void* k_new, const void* v_new, void* 
   pkv::AppendE4m3Args a{k_new, v_new, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
                         k_scale, v_scale, slot_mapping, Hkv, BS};
   return launch_status(pkv::launch_append_e4m3(a, T, D, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int pkv_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (buf == nullptr || sink == nullptr || bytes < 0 || bytes % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return PKV_EINVAL;
+  if (bytes == 0) return PKV_OK;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return launch_status(pkv::launch_stream_read(buf, bytes, sink, cus,
+                                               static_cast<hipStream_t>(stream)));
 }

@@ -222,6 +222,45 @@ def generate(cfg: DecodeConfig, *, seed: int | None = None) -> dict:
     return out
 
 
+def contiguous_layout(cfg: DecodeConfig, d: dict) -> dict:
+    """The same batch with every sequence's blocks made physically
+    consecutive: physical ids are handed out in order of first use in the
+    tables (row by row), so a sequence's private blocks are adjacent and in
+    logical order, and a shared prefix is stored once, ahead of the first
+    sequence that uses it.  Unused table entries point at a poison block
+    (the last id).  Same logical KV, same q and new rows: only the placement
+    changes, which is what measures the cost of paging itself."""
+    BS = cfg.block_size
+    tables, lens = d["block_tables"], d["context_lens"]
+    B = tables.shape[0]
+    new_id = {}
+    order = []
+    for b in range(B):
+        for i in range(-(-int(lens[b]) // BS)):
+            old = int(tables[b, i])
+            if old not in new_id:
+                new_id[old] = len(order)
+                order.append(old)
+    used = len(order)
+    poison = used
+    out = dict(d)
+    out["nb"] = used + 1
+    out["poison_block"] = poison
+    old_ids = np.asarray(order + [int(d["poison_block"])], dtype=np.int64)
+    for key in ("k_pool", "v_pool", "k_scale", "v_scale"):
+        if d.get(key) is not None:
+            out[key] = np.ascontiguousarray(d[key][old_ids])
+    t2 = np.full_like(tables, poison)
+    for b in range(B):
+        n = -(-int(lens[b]) // BS)
+        t2[b, :n] = [new_id[int(x)] for x in tables[b, :n]]
+    out["block_tables"] = t2
+    out["slot_mapping"] = np.array(
+        [int(t2[b, (int(lens[b]) - 1) // BS]) * BS + (int(lens[b]) - 1) % BS if lens[b] > 0
+         else -1 for b in range(B)], dtype=np.int64)
+    return out
+
+
 def kv_bytes(cfg: DecodeConfig, context_lens, window: int = 0) -> int:
     """Algorithmic KV bytes one decode step must read (K and V, plus scales).
     window > 0: only each sequence's last `window` tokens are read."""

@@ -269,3 +269,14 @@ def test_append_e4m3_validation_codes(lib, kw, code):
     assert lib.pkv_validate_append_e4m3(*a.values()) == code
     if code != 0:
         assert lib.paged_kv_append_e4m3(*a.values(), None) == code
+
+
+@pytest.mark.parametrize("buf,nbytes,sink", [
+    (None, 16, A),      # null buffer
+    (A, 16, None),      # null sink
+    (MIS, 16, A),       # misaligned buffer
+    (A, 24, A),         # not a multiple of 16 bytes
+    (A, -16, A),        # negative size
+])
+def test_stream_read_rejects_bad_arguments_before_any_launch(lib, buf, nbytes, sink):
+    assert lib.pkv_stream_read(buf, nbytes, sink, None) == -1

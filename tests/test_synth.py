@@ -84,3 +84,28 @@ def test_kv_bytes():
     cfg = synth.CONFIGS["c2"]
     assert synth.kv_bytes(cfg, [10, 6]) == 16 * 8 * 128 * 2 * 2
     assert synth.kv_bytes(synth.CONFIGS["c5"], [16]) == 16 * 8 * 128 * 2 + 8 * 2 * 4
+
+
+def test_contiguous_layout_keeps_the_logical_kv_and_packs_each_sequence():
+    """The relayout used to price paging: every sequence reads the same
+    logical rows, its private blocks are consecutive and ascending, a shared
+    prefix is stored once, and the new slots point at the same logical
+    position (L - 1)."""
+    cfg = synth.CONFIGS["c3"].replace(B=6, len_hi=100, mbs=70)
+    d = synth.generate(cfg)
+    c = synth.contiguous_layout(cfg, d)
+    prefix = cfg.prefix_tokens // 16
+    for b in range(cfg.B):
+        L = int(d["context_lens"][b])
+        n = -(-L // 16)
+        old = d["k_pool"][d["block_tables"][b, :n]].view(np.uint16)
+        new = c["k_pool"][c["block_tables"][b, :n]].view(np.uint16)
+        assert np.array_equal(old, new)
+        own = c["block_tables"][b, prefix:n]
+        assert np.all(np.diff(own) == 1)
+        assert np.all(c["block_tables"][b, n:] == c["poison_block"])
+        s = int(c["slot_mapping"][b])
+        assert c["block_tables"][b, (L - 1) // 16] == s // 16 and s % 16 == (L - 1) % 16
+    assert np.array_equal(c["block_tables"][:, :prefix], np.tile(np.arange(prefix), (cfg.B, 1)))
+    assert c["nb"] == prefix + sum(-(-(int(L) - cfg.prefix_tokens) // 16)
+                                   for L in d["context_lens"]) + 1
