@@ -156,3 +156,23 @@ def test_fullsize_block32():
     ref = attn_ref(d["q"], kp, vp, d["block_tables"], d["context_lens"], cfg.scale,
                    block_size=32)
     assert max_abs(out, ref) <= TOL_F16
+
+
+def test_fullsize_byte_offsets_past_2gib():
+    """Eight 128K-token sequences, 8 kv heads: 65 K physical blocks, so the
+    pools are 2.1 GB each and tile byte offsets run past 2^31.  Sampled
+    sequences against the oracle, the appended rows read back at their slots."""
+    L = 1 << 17
+    cfg, d = batch("c2", B=8, len_lo=L, len_hi=L, mbs=L // 16)
+    assert int(d["nb"]) * cfg.Hkv * 16 * cfg.D * 2 > 2**31
+    g = to_device(d)
+    out = _run(cfg, g, 64, reps=1)
+    slots = d["slot_mapping"]
+    for b in range(cfg.B):
+        blk, off = divmod(int(slots[b]), 16)
+        assert np.array_equal(_u16(g["k_pool"][blk, :, off].cpu().numpy()), _u16(d["k_new"][b]))
+        assert np.array_equal(_u16(g["v_pool"][blk, :, off].cpu().numpy()), _u16(d["v_new"][b]))
+    kp, vp = append_ref(d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], slots)
+    seqs = [0, cfg.B - 1]
+    ref = attn_ref(d["q"], kp, vp, d["block_tables"], d["context_lens"], cfg.scale, seqs=seqs)
+    assert max_abs(out[seqs], ref[seqs]) <= TOL_F16
