@@ -42,7 +42,8 @@ ROTATE_BYTES = 1 << 30
 # what the counter reads for a plain 256 MiB copy (x2.0 and x1.0).  Keyed by
 # workload and a hash of the step kernel's sources: a changed kernel reports
 # traffic null until it is measured again.
-STEP_SOURCES = ("decode_stream.hip", "decode_tile.h", "device.h", "kernels.h", "shape_limits.h")
+STEP_SOURCES = ("decode_stream.hip", "decode_stream_cached.hip", "decode_stream_impl.h",
+                "decode_tile.h", "device.h", "kernels.h", "shape_limits.h")
 MEASURED_TRAFFIC = {
     ("c2", "ba24803cc25b61af"): {"fetch_bytes": 317760922, "write_bytes": 3321344,
                                  "source": "profiles/step_balanced_c2_hbm_bytes.md"},
@@ -90,6 +91,9 @@ def parse():
     p.add_argument("--paging-overhead", action="store_true",
                    help="also time the same steps with every sequence's blocks made "
                         "physically consecutive, and report the cost of paging itself")
+    p.add_argument("--shared-blocks", default="auto", choices=("auto", "yes", "no"),
+                   help="pass the shared-blocks cache hint (auto: when the workload's tables "
+                        "share a prefix)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after timing, run plain device copies of this many MiB (a known-size "
                         "kernel that profiler byte counters can be scaled against)")
@@ -371,6 +375,10 @@ def main():
 
     ev = {}
 
+    # the caller's block manager knows when tables share blocks (reference
+    # counts); the hint only picks the KV loads' cache policy
+    shared = (cfg.prefix_tokens > 0) if args.shared_blocks == "auto" else args.shared_blocks == "yes"
+
     def step_unfused(g, i, timed):
         if not fp8:
             kw = {}
@@ -385,7 +393,8 @@ def main():
                                g["block_tables"], g["context_lens"], cfg.scale,
                                k_scale=g.get("k_scale"), v_scale=g.get("v_scale"),
                                partition_size=PS, part_out=ws and ws[0],
-                               part_max=ws and ws[1], part_sum=ws and ws[2], stream=stream)
+                               part_max=ws and ws[1], part_sum=ws and ws[2],
+                               shared_blocks=shared, stream=stream)
         if timed:
             ev["d1"][i].record(stream)
         if PS:
@@ -404,7 +413,8 @@ def main():
         _lib.paged_decode_step(out, g["q"], g["k_pool"], g["v_pool"], g["block_tables"],
                                g["context_lens"], cfg.scale, k_scale=g.get("k_scale"),
                                v_scale=g.get("v_scale"), partition_size=step_ps,
-                               window=args.window, workspace=step_ws, stream=stream, **kw)
+                               window=args.window, workspace=step_ws, shared_blocks=shared,
+                               stream=stream, **kw)
         if timed:
             ev["d1"][i].record(stream)
 
@@ -533,6 +543,7 @@ def main():
             "window": args.window,
             "new_tokens_per_sequence": nq,
             "rotated_copies": R,
+            "kv_load_policy": "cached (shared-blocks hint)" if shared else "non-temporal",
         },
         "steps_per_s": round(1e3 / ms, 1),
         "tokens_per_s": round(cfg.B * nq * 1e3 / ms, 1),

@@ -68,6 +68,20 @@ typedef enum {
 typedef enum { PKV_KV_F16 = 0, PKV_KV_E4M3 = 1 } pkv_kv_dtype;
 
 /*
+ * PKV_KV_SHARED_BLOCKS - a hint OR-ed into the kv_dtype argument of
+ * paged_attn_decode and paged_decode_step: some physical blocks are mapped by
+ * several sequences' tables in this call (a prefix shared through reference
+ * counts, or the blocks of forked sequences; "Distributed LLM Inference
+ * Serving Platform", sections 2 and 11).  Without it every KV tile is read
+ * once per call and is loaded with the non-temporal (streaming) cache
+ * policy; with it the KV tiles are loaded with the default policy, so that
+ * the later readers of a shared block find it in L2 or the Infinity Cache.
+ * The results are bitwise the same either way; only speed differs.  Any
+ * other bit above the dtype is PKV_EINVAL.
+ */
+enum { PKV_KV_SHARED_BLOCKS = 0x100 };
+
+/*
  * paged_kv_append - write this step's new K/V rows into their pool slots.
  *
  * "Distributed LLM Inference Serving Platform", section 5.1: K/V of new
@@ -108,6 +122,7 @@ int paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_
  * One online softmax per (sequence, kv head) is shared by the g q heads of
  * the group.  With kv_dtype == PKV_KV_E4M3 the pools hold E4M3 codes and
  * k_scale / v_scale [NB][Hkv] give each (block, kv head) tile's scale.
+ * kv_dtype may carry PKV_KV_SHARED_BLOCKS (cache-policy hint, see above).
  *
  * partition_size == 0: single pass; out [B][Hq][D] fp16 is written
  *   (L_b == 0 gives a zero row); the part_* pointers are ignored.
@@ -187,7 +202,8 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
  *   so (Hq / Hkv) * n_query must be a power of two <= 16.  Balanced split
  *   only, no QK-norm, no window (else PKV_EUNSUPPORTED); part_* then hold
  *   [B][n_query * Hq][max_partitions]([D]).  L_b must be 0 or >= n_query.
- * kv_dtype PKV_KV_E4M3: attend + combine only (k_new must be NULL).
+ * kv_dtype PKV_KV_E4M3: attend + combine only (k_new must be NULL); either
+ *   dtype may carry PKV_KV_SHARED_BLOCKS.
  * L_b == 0: zero output row, nothing written to the pools, q untouched.
  * Errors and shape limits as for paged_attn_decode and paged_kv_append.
  */

@@ -20,6 +20,7 @@ LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_HERE, "libpagedkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH = 0, -1, -2, -3
 PKV_KV_F16, PKV_KV_E4M3 = 0, 1
+PKV_KV_SHARED_BLOCKS = 0x100  # cache-policy hint OR-ed into kv_dtype
 BLOCK_SIZE = 16
 
 _lib = None
@@ -220,11 +221,12 @@ def alloc_partials(B, Hq, D, max_partitions, device="cuda"):
 
 def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, *,
                       k_scale=None, v_scale=None, partition_size=0, part_out=None,
-                      part_max=None, part_sum=None, stream=None):
+                      part_max=None, part_sum=None, shared_blocks=False, stream=None):
     """Decode attention over the paged KV.  partition_size == 0 writes
-    ``out``; otherwise the per-partition workspace is written."""
+    ``out``; otherwise the per-partition workspace is written.
+    shared_blocks: some blocks are mapped by several tables (cache hint)."""
     _check(q, "q", torch.float16, 3)
-    kv = _kv_dtype(k_pool)
+    kv = _kv_dtype(k_pool) | (PKV_KV_SHARED_BLOCKS if shared_blocks else 0)
     _check(k_pool, "k_pool", k_pool.dtype, 4)
     _check(v_pool, "v_pool", k_pool.dtype, 4)
     _check(block_tables, "block_tables", torch.int32, 2)
@@ -236,7 +238,7 @@ def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale,
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables / context_lens must have B rows")
     MBS = block_tables.shape[1]
-    if kv == PKV_KV_E4M3:
+    if (kv & ~PKV_KV_SHARED_BLOCKS) == PKV_KV_E4M3:
         _check(k_scale, "k_scale", torch.float32, 2)
         _check(v_scale, "v_scale", torch.float32, 2)
         if k_scale.shape != (NB, Hkv) or v_scale.shape != (NB, Hkv):
@@ -284,11 +286,13 @@ def workspace_size(B, Hq, D, max_partitions) -> int:
 
 
 def decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale, *, k_scale=None,
-                v_scale=None, partition_size=0, workspace=None, stream=None):
+                v_scale=None, partition_size=0, workspace=None, shared_blocks=False,
+                stream=None):
     """Decode, followed by the reduce when partitioned (same stream)."""
     if partition_size == 0:
         paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale,
-                          k_scale=k_scale, v_scale=v_scale, stream=stream)
+                          k_scale=k_scale, v_scale=v_scale, shared_blocks=shared_blocks,
+                          stream=stream)
         return
     if workspace is None:
         P = max_partitions_for(block_tables.shape[1], partition_size)
@@ -296,7 +300,8 @@ def decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale, *, k_
     po, pm, ps = workspace
     paged_attn_decode(None, q, k_pool, v_pool, block_tables, context_lens, scale,
                       k_scale=k_scale, v_scale=v_scale, partition_size=partition_size,
-                      part_out=po, part_max=pm, part_sum=ps, stream=stream)
+                      part_out=po, part_max=pm, part_sum=ps, shared_blocks=shared_blocks,
+                      stream=stream)
     paged_attn_reduce(out, po, pm, ps, context_lens, partition_size, stream=stream)
 
 
@@ -311,12 +316,13 @@ def alloc_step_workspace(B, Hq, Hkv, D, max_partitions, device="cuda"):
 def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale, *, k_new=None,
                       v_new=None, k_scale=None, v_scale=None, partition_size=0, window=0,
                       gamma_q=None, gamma_k=None, eps=1e-6, rope_theta=1e6, workspace=None,
-                      stream=None):
+                      shared_blocks=False, stream=None):
     """Append (optional, + Qwen3 QK-norm/RoPE) + decode + combine in one launch.
     ``workspace`` is alloc_step_workspace(...)'s tuple.  partition_size 0
     splits contexts evenly over all waves into at most workspace-depth
     pieces; > 0 uses fixed partitions.  window > 0 attends to the last
-    `window` tokens only (balanced split)."""
+    `window` tokens only (balanced split).  shared_blocks: some blocks are
+    mapped by several tables (a shared prefix, forks): a cache-policy hint."""
     nq = 1
     if q.dim() == 4:                      # [B, nq, Hq, D]: several new tokens per sequence
         nq = q.shape[1]
@@ -325,7 +331,7 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
         q3, out3 = q, out
     _check(out3, "out", torch.float16, 3)
     _check(q3, "q", torch.float16, 3)
-    kv = _kv_dtype(k_pool)
+    kv = _kv_dtype(k_pool) | (PKV_KV_SHARED_BLOCKS if shared_blocks else 0)
     _check(k_pool, "k_pool", k_pool.dtype, 4)
     _check(v_pool, "v_pool", k_pool.dtype, 4)
     _check(block_tables, "block_tables", torch.int32, 2)
@@ -337,7 +343,7 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
         raise ValueError("q / out / pool shapes disagree")
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables / context_lens must have B rows")
-    if kv == PKV_KV_E4M3:
+    if (kv & ~PKV_KV_SHARED_BLOCKS) == PKV_KV_E4M3:
         _check(k_scale, "k_scale", torch.float32, 2)
         _check(v_scale, "v_scale", torch.float32, 2)
     if k_new is not None:

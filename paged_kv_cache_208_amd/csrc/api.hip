@@ -53,8 +53,9 @@ extern "C" int paged_attn_decode(void* out, const void* q, const void* k_pool, c
                                      partition_size, part_out, part_max, part_sum,
                                      max_partitions);
   if (st != PKV_OK || B == 0) return st;
-  const bool fp8 = kv_dtype == PKV_KV_E4M3;
+  const bool fp8 = (kv_dtype & ~PKV_KV_SHARED_BLOCKS) == PKV_KV_E4M3;
   pkv::DecodeArgs a{};
+  a.cached_kv = (kv_dtype & PKV_KV_SHARED_BLOCKS) != 0;
   a.out = out;
   a.q = q;
   a.k_pool = static_cast<const uint8_t*>(k_pool);
@@ -107,8 +108,9 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
                                    eps, rope_theta, part_out, part_max, part_sum, counters,
                                    max_partitions);
   if (st != PKV_OK || B == 0) return st;
-  const bool fp8 = kv_dtype == PKV_KV_E4M3;
+  const bool fp8 = (kv_dtype & ~PKV_KV_SHARED_BLOCKS) == PKV_KV_E4M3;
   pkv::DecodeArgs a{};
+  a.cached_kv = (kv_dtype & PKV_KV_SHARED_BLOCKS) != 0;
   a.out = out;
   a.q = q;
   a.k_pool = static_cast<const uint8_t*>(k_pool);

@@ -249,7 +249,7 @@ __device__ __forceinline__ void load_mtile(MTile<D, FP8>& t, const DecodeArgs& a
                                            int k, const Unit& u, int k_off, int v_off) {
   size_t base;
   const int rows = tile_base<MfmaGeo<D, FP8>::kTile, NW>(a, walk, k, u, base);
-  load_mtile_at<D, FP8>(t, a, base, rows, k_off, v_off);
+  load_mtile_at<D, FP8>(t, a, base, rows, k_off, v_off, a.cached_kv != 0);
 }
 
 template <int D, int G, bool FP8, int NW, int MODE>
@@ -451,10 +451,17 @@ __device__ __forceinline__ void load_tile(TileRegs<D, FP8>& t, const DecodeArgs&
   const int nbytes = t.rows * Geo::kRow;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_pool + base, nbytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_pool + base, nbytes);
+  if (a.cached_kv) {
 #pragma unroll
-  for (int i = 0; i < Geo::kNi; ++i) t.k[i] = buffer_load16(rk, lane_off + i * Geo::kTpi * Geo::kRow);
+    for (int i = 0; i < Geo::kNi; ++i) t.k[i] = buffer_load16(rk, lane_off + i * Geo::kTpi * Geo::kRow);
 #pragma unroll
-  for (int i = 0; i < Geo::kNi; ++i) t.v[i] = buffer_load16(rv, lane_off + i * Geo::kTpi * Geo::kRow);
+    for (int i = 0; i < Geo::kNi; ++i) t.v[i] = buffer_load16(rv, lane_off + i * Geo::kTpi * Geo::kRow);
+  } else {
+#pragma unroll
+    for (int i = 0; i < Geo::kNi; ++i) t.k[i] = buffer_load16_kv(rk, lane_off + i * Geo::kTpi * Geo::kRow);
+#pragma unroll
+    for (int i = 0; i < Geo::kNi; ++i) t.v[i] = buffer_load16_kv(rv, lane_off + i * Geo::kTpi * Geo::kRow);
+  }
   t.ks = t.vs = 1.0f;
   if constexpr (FP8) {
     if (t.rows > 0) {

@@ -34,6 +34,7 @@ struct DecodeArgs {
   int group;                  // Hq / Hkv
   int bs_tiles;               // 16-token tiles per block: 1, or 2 for 32-token blocks
   int bs_shift;               // log2(bs_tiles)
+  int cached_kv;              // nonzero: KV tiles with the default cache policy (shared blocks)
 };
 
 // What a decode launch does besides attending (bit flags).
@@ -102,6 +103,9 @@ hipError_t launch_decode_step(const DecodeArgs& a, int B, int D, int group, bool
 // cols = (Hq / Hkv) * nq, the used columns of the 16-wide products (1..16)
 hipError_t launch_decode_stream(const DecodeArgs& a, int B, int D, int cols, bool fp8, int mode,
                                 hipStream_t stream);
+// the same with the default cache policy for the KV tiles (shared-blocks hint)
+hipError_t launch_decode_stream_cached(const DecodeArgs& a, int B, int D, int cols, bool fp8,
+                                       int mode, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int B, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int T, int D, bool fused, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t stream);

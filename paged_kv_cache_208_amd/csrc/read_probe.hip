@@ -3,7 +3,9 @@
 //
 // Each wave owns one contiguous span of the buffer and reads it 1 KiB per
 // load instruction (lane i takes the i-th 16 bytes), 16 instructions in
-// flight; 32 four-wave workgroups per CU.  Of the shapes measured on this
+// flight; 32 four-wave workgroups per CU.  The loads are non-temporal, as the
+// decode kernels' KV loads are (5.9 TB/s with the default policy, 6.8 with
+// this one, 1 GiB).  Of the shapes measured on this
 // GPU (grid-stride loops with 4-16 loads in flight, spans with 8-16, 4-32
 // workgroups per CU) this one read fastest.  The loaded words are
 // XOR-folded and the fold is stored only if it equals a value it cannot
@@ -33,7 +35,7 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* 
 #pragma unroll
     for (int k = 0; k < kReadDepth; ++k) {
       const int64_t i = (r + k) * kWave + lane;
-      v[k] = r + k < r1 && i < n16 ? buf[i] : u32x4{0u, 0u, 0u, 0u};
+      v[k] = r + k < r1 && i < n16 ? __builtin_nontemporal_load(&buf[i]) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int k = 0; k < kReadDepth; ++k) acc ^= v[k];

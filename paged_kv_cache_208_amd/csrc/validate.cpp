@@ -78,6 +78,7 @@ extern "C" int pkv_validate_decode(const void* out, const void* q, const void* k
     return PKV_EINVAL;
   if (Hq % Hkv != 0) return PKV_EINVAL;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return PKV_EINVAL;
+  kv_dtype &= ~PKV_KV_SHARED_BLOCKS;  // a cache-policy hint, not part of the dtype
   if (kv_dtype != PKV_KV_F16 && kv_dtype != PKV_KV_E4M3) return PKV_EINVAL;
   if (partition_size < 0) return PKV_EINVAL;
   if (!supported_head_dim(D) || !supported_group(Hq / Hkv)) return PKV_EUNSUPPORTED;
@@ -174,7 +175,7 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
       return PKV_EUNSUPPORTED;
   }
   if (k_new != nullptr) {
-    if (kv_dtype != PKV_KV_F16) return PKV_EUNSUPPORTED;
+    if ((kv_dtype & ~PKV_KV_SHARED_BLOCKS) != PKV_KV_F16) return PKV_EUNSUPPORTED;
     if (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return PKV_EINVAL;
   } else if (v_new != nullptr) {
     return PKV_EINVAL;

@@ -89,6 +89,11 @@ def _validate_decode(lib, **kw):
     (dict(kv_dtype=2), -1),
     (dict(kv_dtype=1), -1),
     (dict(kv_dtype=1, k_scale=A, v_scale=A), 0),
+    (dict(kv_dtype=0x100), 0),                           # shared-blocks hint, fp16
+    (dict(kv_dtype=0x101, k_scale=A, v_scale=A), 0),     # hint with E4M3
+    (dict(kv_dtype=0x101), -1),                          # E4M3 still needs its scales
+    (dict(kv_dtype=0x200), -1),                          # an unknown bit
+    (dict(kv_dtype=0x102), -1),
     (dict(partition_size=-16), -1),
     (dict(partition_size=24, part_out=A, part_max=A, part_sum=A, max_partitions=8), -2),
     (dict(partition_size=32768, part_out=A, part_max=A, part_sum=A, max_partitions=8), -2),
@@ -215,6 +220,10 @@ def _step_args(**kw):
     (dict(gamma_k=A, gamma_q=A, theta=-1.0), -1),
     (dict(kv_dtype=1, k_scale=A, v_scale=A), -2),
     (dict(kv_dtype=1, k_scale=A, v_scale=A, k_new=None, v_new=None), 0),
+    (dict(kv_dtype=0x100), 0),                           # shared-blocks hint with the append
+    (dict(kv_dtype=0x101, k_scale=A, v_scale=A), -2),    # E4M3 does not append
+    (dict(kv_dtype=0x101, k_scale=A, v_scale=A, k_new=None, v_new=None), 0),
+    (dict(kv_dtype=0x300), -1),
     (dict(D=96), -2),
     (dict(max_partitions=1), -1),
     (dict(partition_size=16, MBS=65, max_partitions=65), -2),
@@ -239,6 +248,7 @@ def test_step_validation_codes(lib, kw, code):
     (dict(kv_dtype=2), -1),
     (dict(kv_dtype=1), -1),
     (dict(kv_dtype=1, k_scale=A, v_scale=A), 0),
+    (dict(kv_dtype=0x100), -1),                          # the hint is for the readers only
     (dict(NB=0), -1),
 ])
 def test_copy_validation_codes(lib, kw, code):
