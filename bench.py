@@ -45,7 +45,7 @@ ROTATE_BYTES = 1 << 30
 STEP_SOURCES = ("decode_stream.hip", "decode_stream_cached.hip", "decode_stream_impl.h",
                 "decode_tile.h", "device.h", "kernels.h", "shape_limits.h")
 MEASURED_TRAFFIC = {
-    ("c2", "ba24803cc25b61af"): {"fetch_bytes": 317760922, "write_bytes": 3321344,
+    ("c2", "dd6e36823f99e885"): {"fetch_bytes": 317698059, "write_bytes": 3321376,
                                  "source": "profiles/step_balanced_c2_hbm_bytes.md"},
 }
 
