@@ -160,3 +160,17 @@ class BlockPool:
 
     def context_lens_array(self, sids) -> np.ndarray:
         return np.array([self.lens[s] for s in sids], dtype=np.int32)
+
+    def shares_blocks(self, sids) -> bool:
+        """True when some physical block is mapped by the tables of two or
+        more of the sequences `sids` (a shared prefix, or forked sequences):
+        the batch then reads that block several times in one decode call,
+        which is when the caller passes the library's shared-blocks cache
+        hint (PKV_KV_SHARED_BLOCKS)."""
+        seen = set()
+        for s in sids:
+            for blk in set(self.tables[s]):
+                if blk in seen:
+                    return True
+                seen.add(blk)
+        return False

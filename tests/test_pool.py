@@ -104,3 +104,23 @@ def test_partial_blocks_cannot_be_shared_as_prefix():
     pool.append_slot("p")
     with pytest.raises(ValueError):
         pool.add_sequence("q", prefix_blocks=pool.tables["p"])
+
+
+def test_shares_blocks_reports_blocks_mapped_by_two_tables_of_the_batch():
+    pool = BlockPool(num_blocks=16)
+    for s in ("x", "y"):
+        pool.add_sequence(s)
+        for _ in range(20):
+            pool.append_slot(s)
+    assert not pool.shares_blocks(["x", "y"])          # private blocks only
+    prefix = list(pool.tables["x"][:1])                 # one full 16-token block
+    pool.add_sequence("z", prefix_blocks=prefix)
+    pool.append_slot("z")
+    assert pool.shares_blocks(["x", "z"])               # z maps x's first block
+    assert not pool.shares_blocks(["y", "z"])
+    assert not pool.shares_blocks(["z"])                # one table never shares with itself
+    pool.fork("y", ["y1"])
+    assert pool.shares_blocks(["y", "y1"])              # forks share every block
+    pool.append_slot("y1")                              # copy-on-write of the tail block
+    assert pool.tables["y1"][-1] != pool.tables["y"][-1]
+    assert pool.shares_blocks(["y", "y1"])              # the full block stays shared
