@@ -261,6 +261,17 @@ def contiguous_layout(cfg: DecodeConfig, d: dict) -> dict:
     return out
 
 
+def unique_kv_bytes(cfg: DecodeConfig, context_lens) -> int:
+    """KV bytes of the distinct blocks a step reads: a shared prefix (every
+    table maps the same prefix_tokens first) is counted once.  Equals
+    kv_bytes when nothing is shared."""
+    lens = np.asarray(context_lens, dtype=np.int64)
+    if cfg.prefix_tokens <= 0 or lens.size == 0:
+        return kv_bytes(cfg, lens)
+    tails = np.maximum(lens - cfg.prefix_tokens, 0)
+    return kv_bytes(cfg, np.concatenate([[cfg.prefix_tokens], tails]))
+
+
 def kv_bytes(cfg: DecodeConfig, context_lens, window: int = 0) -> int:
     """Algorithmic KV bytes one decode step must read (K and V, plus scales).
     window > 0: only each sequence's last `window` tokens are read."""

@@ -109,3 +109,13 @@ def test_contiguous_layout_keeps_the_logical_kv_and_packs_each_sequence():
     assert np.array_equal(c["block_tables"][:, :prefix], np.tile(np.arange(prefix), (cfg.B, 1)))
     assert c["nb"] == prefix + sum(-(-(int(L) - cfg.prefix_tokens) // 16)
                                    for L in d["context_lens"]) + 1
+
+
+def test_unique_kv_bytes_counts_a_shared_prefix_once():
+    cfg = synth.CONFIGS["c3"]
+    lens = np.array([1024 + 16, 1024 + 100, 1024 + 2048])
+    per_token = cfg.Hkv * cfg.D * 2 * 2
+    assert synth.kv_bytes(cfg, lens) == int(lens.sum()) * per_token
+    assert synth.unique_kv_bytes(cfg, lens) == (1024 + 16 + 100 + 2048) * per_token
+    c2 = synth.CONFIGS["c2"]
+    assert synth.unique_kv_bytes(c2, lens) == synth.kv_bytes(c2, lens)   # nothing shared
