@@ -2,13 +2,16 @@
 // the combine of split contexts in one launch, with every wave given the
 // same amount of KV to read.
 //
-// The batch's tiles are laid out in one flattened order: sequence b, then kv
-// head, then the sequence's 16-token tiles ("Distributed LLM Inference
+// The batch's tiles are laid out in one flattened order: kv head, then
+// sequence b, then the sequence's 16-token tiles ("Distributed LLM Inference
 // Serving Platform", section 2: logical block n of a sequence is found
 // through its block table).  With W tiles in total and C waves (a fixed
-// number per CU), wave w reads the contiguous range [w*tpw, (w+1)*tpw),
-// tpw = ceil(W / C) (with two waves per SIMD the first C/2 ranges are a
-// little longer; see Ranges).  Every wave therefore moves about the same
+// number per CU), the ranges are contiguous runs of about W / C tiles (with
+// two waves per SIMD the first-placed waves' ranges are a little longer; see
+// Ranges), and the waves of one XCD take one contiguous block of ranges: an
+// XCD reads about one kv head's tiles, so the blocks that several sequences
+// share (a common prefix) are re-read through that XCD's own L2, and the
+// pieces of a split segment are combined within one XCD.  Every wave therefore moves about the same
 // number of bytes, whatever the mix of context lengths, and streams straight
 // across the boundaries between (sequence, kv head) segments: the next
 // tile's loads are issued before the current tile is computed, whichever
@@ -93,9 +96,10 @@ __device__ __forceinline__ int64_t wave_scan(int64_t x) {
   return x;
 }
 
-// Tiles of the batch (all kv heads) and the most tiles of one sequence.
+// Tiles of the batch (all kv heads), of one kv head, and the most tiles of
+// one sequence.
 struct Totals {
-  int64_t tiles;
+  int64_t tiles, per_head;
   int max_tiles;
 };
 
@@ -114,31 +118,32 @@ __device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B, int L0
   }
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) mx = max(mx, __shfl_xor(mx, off));
-  return Totals{tot * a.Hkv, __builtin_amdgcn_readfirstlane(mx)};
+  return Totals{tot * a.Hkv, tot, __builtin_amdgcn_readfirstlane(mx)};
 }
 
-// Cursor of flattened tile t (t < total).
-__device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, int L0, int W) {
+// Cursor of flattened tile t (t < total); wh = tiles of one kv head.
+__device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, int64_t wh, int L0,
+                                        int W) {
   const int lane = threadIdx.x & (kWave - 1);
   Cursor c{};
+  c.kvh = int(t / wh);
+  const int64_t r = t - int64_t(c.kvh) * wh;  // position within the head's run
   int64_t carry = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
     const int L = c0 == 0 ? L0 : b < B ? a.context_lens[b] : 0;
-    const int64_t w = int64_t(a.Hkv) * seg_tiles(L, W);
+    const int64_t w = seg_tiles(L, W);
     const int64_t hi = carry + wave_scan(w);
     const int64_t lo = hi - w;
-    const uint64_t here = __builtin_amdgcn_ballot_w64(b < B && lo <= t && t < hi);
+    const uint64_t here = __builtin_amdgcn_ballot_w64(b < B && lo <= r && r < hi);
     if (here) {
       const int src = __builtin_ctzll(here);
       c.b = c0 + src;
       c.L = __builtin_amdgcn_readlane(L, src);
       c.T = seg_tiles(c.L, W);
       c.f = first_tile(c.L, W);
-      const int64_t off = t - readlane64(lo, src);
-      c.kvh = int(off / c.T);
-      c.n = int(off % c.T);
-      c.S = readlane64(lo, src) + int64_t(c.kvh) * c.T;
+      c.n = int(r - readlane64(lo, src));
+      c.S = int64_t(c.kvh) * wh + readlane64(lo, src);
       return c;
     }
     carry = readlane64(hi, kWave - 1);
@@ -146,15 +151,20 @@ __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, 
   return c;  // not reached for t < total
 }
 
-// Next tile in the flattened order (skips sequences with no tokens).
+// Next tile in the flattened order (skips sequences with no tokens); past
+// the last tile c.b == B.
 __device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B, int W) {
   if (++c.n < c.T) return;
   c.n = 0;
   c.S += c.T;
-  if (++c.kvh < a.Hkv) return;
-  c.kvh = 0;
   do {
-    if (++c.b >= B) return;
+    if (++c.b >= B) {
+      c.b = 0;
+      if (++c.kvh >= a.Hkv) {
+        c.b = B;
+        return;
+      }
+    }
     c.L = load_uniform(a.context_lens + c.b);
   } while (c.L == 0);
   c.T = seg_tiles(c.L, W);
@@ -165,36 +175,55 @@ __device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B, i
 #define PKV_STREAM_SKEW_FP8 120
 #endif
 
-// The wave ranges: the first H = workers / 2 waves read ranges of ta tiles,
-// the others ranges of tb, back to back in the flattened order.  With two
-// waves per SIMD the first wave placed on a SIMD is served first when both
-// are ready to issue, and equal shares end far apart; the first half then
-// takes the larger share (skew ta : tb, in percent).  Every range is long
-// enough that no sequence is cut into more than P pieces: T tiles span at
-// most (T - 1) / r + 2 ranges of r >= rmin tiles.
+// The wave ranges, back to back in the flattened order, in nblk blocks of
+// per = workers / nblk ranges (one block per XCD when the grid allows it):
+// in each block the first nh = per / 2 ranges hold ta tiles, the others tb.
+// Wave w (on XCD w % nblk) reads range (w % nblk) * per + w / nblk, so an
+// XCD's waves read one contiguous block, and the first half of the waves (w
+// < workers / 2) get the ta ranges.  With two waves per SIMD the first wave
+// placed on a SIMD is served first when both are ready to issue, and equal
+// shares end far apart; that half then takes the larger share (skew ta : tb,
+// in percent).  Every range is long enough that no sequence is cut into more
+// than P pieces: T tiles span at most (T - 1) / r + 2 ranges of r >= rmin
+// tiles.
 struct Ranges {
-  int64_t ta, tb, H;
-  __device__ __forceinline__ int64_t start(int64_t w) const {
-    return w <= H ? w * ta : H * ta + (w - H) * tb;
+  int64_t ta, tb, nh, per, blk;
+  __device__ __forceinline__ int64_t start(int64_t r) const {
+    const int64_t x = r / per, i = r - x * per;
+    return x * blk + (i <= nh ? i * ta : nh * ta + (i - nh) * tb);
   }
   __device__ __forceinline__ int64_t of(int64_t t) const {  // range holding tile t
-    return t < H * ta ? t / ta : H + (t - H * ta) / tb;
+    const int64_t x = t / blk, rem = t - x * blk;
+    return x * per + (rem < nh * ta ? rem / ta : nh + (rem - nh * ta) / tb);
   }
 };
+
+__host__ __device__ constexpr int range_blocks(int workers) {
+  return workers % (2 * kXcds) == 0 ? kXcds : 1;
+}
+
+__device__ __forceinline__ int64_t range_of_worker(int w, int workers) {
+  const int nblk = range_blocks(workers);
+  return int64_t(w % nblk) * (workers / nblk) + w / nblk;
+}
 
 template <bool FP8>
 __device__ __forceinline__ Ranges make_ranges(int64_t W, int Tmax, int workers, int P) {
   const int64_t rmin = max(int64_t(1), int64_t(Tmax + P - 3) / (P - 2));
   const int skew = FP8 ? PKV_STREAM_SKEW_FP8 : 100;
+  const int nblk = range_blocks(workers);
   Ranges r;
-  r.H = workers / 2;
+  r.per = workers / nblk;
+  r.nh = r.per / 2;
   if (skew == 100) {
     r.ta = r.tb = max((W + workers - 1) / workers, rmin);
-    return r;
+  } else {
+    // W * skew / (skew + 100) tiles for the first half
+    const int64_t na = int64_t(nblk) * r.nh, nb = int64_t(nblk) * (r.per - r.nh);
+    r.ta = max((W * skew / (skew + 100) + na - 1) / na, rmin);
+    r.tb = max((max(W - na * r.ta, int64_t(0)) + nb - 1) / nb, rmin);
   }
-  // W * skew / (skew + 100) tiles for the first half
-  r.ta = max((W * skew / (skew + 100) + r.H - 1) / r.H, rmin);
-  r.tb = max((max(W - r.H * r.ta, int64_t(0)) + (workers - r.H) - 1) / (workers - r.H), rmin);
+  r.blk = r.nh * r.ta + (r.per - r.nh) * r.tb;
   return r;
 }
 
@@ -583,11 +612,12 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   // equal shares, but long enough that no sequence's segment is cut into more
   // than max_partitions pieces: T tiles span at most (T-1)/tpw + 2 ranges
   const Ranges rg = make_ranges<FP8>(W, tot.max_tiles, workers, a.max_partitions);
-  const int64_t t0 = min(rg.start(worker), W);
-  const int64_t t1 = min(W, rg.start(worker + 1));
+  const int64_t rw = range_of_worker(worker, workers);  // this wave's range
+  const int64_t t0 = min(rg.start(rw), W);
+  const int64_t t1 = min(W, rg.start(rw + 1));
 
   if (t0 < t1) {
-    Cursor cur = locate(a, B, t0, L0, win);
+    Cursor cur = locate(a, B, t0, tot.per_head, L0, win);
     int rope_b[2] = {-1, -1};  // sequence whose angles are in each table
     int ord = 0;                // segments entered so far; parity picks the table
     if constexpr (K::QKNORM) {
@@ -708,7 +738,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
           pend = true;
           pseg = seg;
           ppieces = pieces;
-          pj = int(worker - rg.of(mx.S));
+          pj = int(rw - rg.of(mx.S));
         }
         K::reset(st);
       }
@@ -733,7 +763,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       if constexpr (K::QKNORM) K::write_q(a, fseg, qop, g, n16);
     } else {
       K::stage_partial(st, l, g, n16, s_fin);
-      K::write_partial(a, size_t(fseg) * C, int(worker - rg.of(mf.S)), s_fin);
+      K::write_partial(a, size_t(fseg) * C, int(rw - rg.of(mf.S)), s_fin);
     }
     if (pend) K::write_partial(a, size_t(pseg) * C, pj, s_pend);
     if (pend || fpieces > 1) {

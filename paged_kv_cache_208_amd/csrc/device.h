@@ -14,6 +14,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kWave = 64;
+// XCDs of an MI355X; the workgroups of a launch are handed to them round-robin
+// (workgroup i runs on XCD i % 8).
+constexpr int kXcds = 8;
 
 // gfx9 buffer resource word 3 for raw (untyped, stride 0) dword access.
 constexpr int kRawBufferFlags = 0x00020000;
