@@ -357,3 +357,28 @@ def test_step_multi_token_e4m3():
     ref = mq_attn_ref(q, d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
                       cfg.scale, k_scale=d["k_scale"], v_scale=d["v_scale"])
     assert max_abs(out, ref) <= TOL_E4M3
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (16, 2), (32, 8)])
+def test_step_balanced_head_wrap_with_empty_ends(Hq, Hkv):
+    """The balanced split orders tiles kv head first: a wave's range runs from
+    the last sequences of one head into the first sequences of the next.
+    Empty sequences at both ends of the batch (and B > 64) make the cursor
+    skip them across that wrap; splits=3 makes the ranges long enough to
+    cross several heads."""
+    cfg, d = batch("c2", B=70, Hq=Hq, Hkv=Hkv, D=128, len_lo=1, len_hi=120, mbs=8)
+    lens = d["context_lens"].copy()
+    lens[[0, 1, 35, 68, 69]] = 0
+    keep = lens > 0
+    slots = np.where(keep, d["slot_mapping"], -1)
+    d2 = dict(d, context_lens=lens)
+    for splits in (3, 16):
+        g = to_device(d2)
+        out, ws = _step(cfg, g, 0, splits=splits)
+        kp, vp = append_ref(d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], slots)
+        assert np.array_equal(_u16(g["k_pool"].cpu().numpy()), _u16(kp))
+        assert np.array_equal(_u16(g["v_pool"].cpu().numpy()), _u16(vp))
+        ref = attn_ref(d["q"], kp, vp, d["block_tables"], lens, cfg.scale)
+        assert torch.all(out[~torch.from_numpy(keep).cuda()] == 0)
+        assert max_abs(out, ref) <= TOL_F16
+        assert torch.count_nonzero(ws[3]).item() == 0
