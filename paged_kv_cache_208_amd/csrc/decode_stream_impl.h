@@ -597,10 +597,12 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   __shared__ float s_w[2 * C * kMaxStepPartitions];  // combine weights
   __shared__ float s_fin[K::kStage];                  // the range's last piece
   __shared__ float s_pend[K::kStage];                 // a piece that ended earlier
-  // rotation angles of two segments' positions: the segment being computed
-  // and the next one being prepared (QK-norm modes)
-  __shared__ float s_cos[K::QKNORM ? 2 * (D / 2) : 1];
-  __shared__ float s_sin[K::QKNORM ? 2 * (D / 2) : 1];
+  // rotation angles of the positions of up to kDepth segments (QK-norm
+  // modes): a segment's table is written when its first tile is issued and
+  // read when that tile is computed, and at most kDepth - 1 tiles are issued
+  // in between, so kDepth tables taken in turn never overwrite one in use
+  __shared__ float s_cos[K::QKNORM ? K::kDepth * (D / 2) : 1];
+  __shared__ float s_sin[K::QKNORM ? K::kDepth * (D / 2) : 1];
   __shared__ _Float16 s_q[K::QKNORM ? C * D : 1];
   __shared__ double s_f[K::QKNORM ? D / 2 : 1];      // rotation frequencies
   __shared__ float s_gq[K::QKNORM ? D : 1];          // RMSNorm weights of q and k
@@ -618,8 +620,10 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
 
   if (t0 < t1) {
     Cursor cur = locate(a, B, t0, tot.per_head, L0, win);
-    int rope_b[2] = {-1, -1};  // sequence whose angles are in each table
-    int ord = 0;                // segments entered so far; parity picks the table
+    int rope_b[K::kDepth];  // sequence whose angles are in each table
+#pragma unroll
+    for (int i = 0; i < K::kDepth; ++i) rope_b[i] = -1;
+    int ord = 0;  // segments entered so far; picks the table in turn
     if constexpr (K::QKNORM) {
       rope_freqs<D>(s_f, a.theta);
       for (int i = lane; i < D; i += kWave) {
@@ -630,7 +634,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
     if constexpr (K::APPEND)
       K::append_rows(a, B, cur, t0, t1, g, n16, k_off, v_off, s_cos, s_sin, s_f, s_gk);
     auto prepare_segment = [&](Meta& m) {
-      m.slot = ord++ & 1;
+      m.slot = ord++ % K::kDepth;
       if constexpr (K::QKNORM) {
         if (m.b != rope_b[m.slot]) {
           rope_angles<D>(s_f, s_cos + m.slot * (D / 2), s_sin + m.slot * (D / 2), m.L - 1);
