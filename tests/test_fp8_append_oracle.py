@@ -46,26 +46,33 @@ def _half_spacing(v):
     return np.where(a < 2.0 ** -6, 2.0 ** -10, 2.0 ** (e - 4))
 
 
-def _one_block(rows, Hkv=2, D=32, stale=None):
-    """Append `rows` ([n][Hkv][D] fp16) one per call into block 3 of a pool."""
+def _one_block(rows, Hkv=2, D=32, stale=None, bs=16):
+    """Append `rows` ([n][Hkv][D] fp16) one per call into block 3 of a pool
+    of `bs`-token blocks."""
     NB = 6
-    kp = np.zeros((NB, Hkv, 16, D), dtype=np.uint8) if stale is None else stale.copy()
+    kp = np.zeros((NB, Hkv, bs, D), dtype=np.uint8) if stale is None else stale.copy()
     vp = kp.copy()
     ks = np.full((NB, Hkv), 7.0, dtype=F32)    # stale scales: a new block ignores them
     vs = ks.copy()
     hist = []
     for r, x in enumerate(rows):
         kp, vp, ks, vs = append_e4m3_ref(kp, vp, ks, vs, x[None], x[None],
-                                         np.array([3 * 16 + r], dtype=np.int64))
+                                         np.array([3 * bs + r], dtype=np.int64), block_size=bs)
         hist.append((kp.copy(), ks.copy()))
     return hist
 
 
-def test_scale_tracks_running_amax_and_values_stay_within_rounding():
+@pytest.mark.parametrize("bs", [16, 32])
+def test_scale_tracks_running_amax_and_values_stay_within_rounding(bs):
+    """bs = 32: the same policy over a 32-token block ("Distributed LLM
+    Inference Serving Platform", section 12), slots block * 32 + row."""
     rng = np.random.default_rng(3)
     mags = [0.5, 2.0, 1.0, 40.0, 3.0, 300.0, 0.01, 300.0, 1e-3, 7.0, 7.0, 90.0, 1.0, 2.0, 0.0, 500.0]
+    if bs == 32:
+        mags = mags + [0.2, 600.0, 1.0, 1e-2, 5.0, 5.0, 0.0, 700.0, 3.0, 2.0, 1.0, 40.0, 8.0, 9.0,
+                       0.5, 1.0]
     rows = [(rng.standard_normal((2, 32)) * m).astype(np.float16) for m in mags]
-    hist = _one_block(rows)
+    hist = _one_block(rows, bs=bs)
     tab = e4m3_table()
     prev_codes = prev_scale = None
     for r, (kp, ks) in enumerate(hist):
@@ -91,8 +98,8 @@ def test_scale_tracks_running_amax_and_values_stay_within_rounding():
     for h in range(2):
         s = float(ks[3, h])
         scales = [float(hs[3, h]) for _, hs in hist]
-        for r in range(16):
-            k = sum(1 for j in range(r + 1, 16) if scales[j] != scales[j - 1])
+        for r in range(bs):
+            k = sum(1 for j in range(r + 1, bs) if scales[j] != scales[j - 1])
             x = rows[r][h].astype(np.float64)
             got = tab[kp[3, h, r]] * s
             bound = (k + 1) * (2.0 ** -4 * np.abs(x) * 1.1 + 2.0 ** -10 * s)

@@ -2,10 +2,13 @@
 
 The table is built from the format's closed form in oracle/e4m3.py; here it
 is checked code by code against torch's independent float8_e4m3fn decoder,
-and against landmark values of the OCP E4M3 definition written out by hand.
+and against landmark values of the OCP E4M3 definition worked out by hand
+from the bit fields (tests/golden/e4m3_landmarks.json).
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import torch
@@ -36,6 +39,19 @@ def test_landmarks_of_the_format():
     assert math.isnan(t[0x7F]) and math.isnan(t[0xFF])
     assert np.nanmax(np.abs(t)) == 448.0
     assert np.sum(np.isnan(t)) == 2
+
+
+def test_hand_worked_landmark_codes(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "e4m3_landmarks.json")))
+    t = e4m3_table()
+    assert len(g["codes"]) >= 12
+    for c in g["codes"]:
+        code = int(c["code"], 16)
+        if c["value"] == "nan":
+            assert math.isnan(t[code]), c
+        else:
+            assert t[code] == c["value"], c
+            assert math.copysign(1, t[code]) == math.copysign(1, c["value"]), c
 
 
 def test_positive_codes_are_monotone_and_sign_symmetric():
