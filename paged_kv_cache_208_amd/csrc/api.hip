@@ -6,22 +6,10 @@
 #include "device.h"
 #include "shape_limits.h"
 
-#include <cstdlib>
-#include <cstring>
 
 namespace {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
-
-// Decode tile engine: MFMA unless PKV_DECODE_ENGINE=valu (read once).
-pkv::DecodeEngine decode_engine() {
-  static const pkv::DecodeEngine engine = [] {
-    const char* s = std::getenv("PKV_DECODE_ENGINE");
-    return (s != nullptr && std::strcmp(s, "valu") == 0) ? pkv::DecodeEngine::kValu
-                                                          : pkv::DecodeEngine::kMfma;
-  }();
-  return engine;
-}
 
 }  // namespace
 
@@ -77,7 +65,7 @@ extern "C" int paged_attn_decode(void* out, const void* q, const void* k_pool, c
   a.max_partitions = partition_size ? max_partitions : 1;
   a.scale_log2 = scale * pkv::kLog2e;
   return launch_status(
-      pkv::launch_decode(a, B, D, Hq / Hkv, fp8, decode_engine(), static_cast<hipStream_t>(stream)));
+      pkv::launch_decode(a, B, D, Hq / Hkv, fp8, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int paged_attn_reduce(void* out, const float* part_out, const float* part_max,

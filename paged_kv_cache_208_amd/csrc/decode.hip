@@ -18,16 +18,12 @@
 // logits of those rows are replaced by -inf before the softmax, so pad rows
 // holding anything (NaN included) cannot reach the output.
 //
-// Two tile engines compute the same thing:
-//  * MFMA (default): S^T = K Q^T with v_mfma_f32_16x16x32_f16 (16 tokens x
-//    16 head slots, the g real heads padded with zero queries), then
-//    O^T += V^T P^T with v_mfma_f32_16x16x16_f16.  The QK result layout is
-//    exactly the B-operand layout the PV product needs, so P never leaves
-//    the registers; V is regrouped into token-major quads with byte
-//    permutes.  About 50 VALU instructions per fp16 tile.
-//  * VALU: 16-byte K/V slices per lane, v_dot2 partial logits completed by
-//    DPP row reductions, fp32 FMAs for P.V.  About 430 VALU instructions
-//    per fp16 tile.
+// Tile engine (MFMA): S^T = K Q^T with v_mfma_f32_16x16x32_f16 (16 tokens x
+// 16 head slots, the g real heads padded with zero queries), then
+// O^T += V^T P^T with v_mfma_f32_16x16x16_f16.  The QK result layout is
+// exactly the B-operand layout the PV product needs, so P never leaves the
+// registers; V is regrouped into token-major quads with byte permutes.
+// About 50 VALU instructions per fp16 tile.
 #include <type_traits>
 
 #include "decode_tile.h"
@@ -50,9 +46,6 @@
 
 #define PKV_DECODE_BOUNDS(NW) \
   __launch_bounds__((NW) * kWave) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, 8)))
-// the VALU engine keeps its whole g x D/4 accumulator in registers: no
-// occupancy target, so large groups do not spill
-#define PKV_DECODE_VALU_BOUNDS(NW) __launch_bounds__((NW) * kWave)
 
 namespace pkv {
 namespace {
@@ -411,251 +404,6 @@ __global__ PKV_DECODE_BOUNDS(NW) void decode_mfma_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// VALU engine.
-//
-// A token row of one head is ROW = D * bytes long and is read by
-// LPT = ROW / 16 lanes with one 16-byte load each, so one wave load covers
-// TPI = 64 / LPT consecutive rows (a contiguous 1 KiB) and a tile takes
-// NI = 16 / TPI loads.  Each lane dots its 16 bytes of K with the matching
-// slice of the g query heads; a DPP reduction inside the LPT-lane group
-// completes the logit.  Every lane group keeps its own running max / sum /
-// accumulator; groups and waves are merged once at the end of the unit.
-
-template <int D, bool FP8>
-struct Geometry {
-  static constexpr int kBytes = FP8 ? 1 : 2;
-  static constexpr int kRow = D * kBytes;
-  static constexpr int kLpt = kRow / 16;
-  static constexpr int kTpi = kWave / kLpt;
-  static constexpr int kNi = 16 / kTpi;
-  static constexpr int kEpl = 16 / kBytes;
-  static constexpr int kTile = 16 * kRow;
-  static_assert(kLpt >= 4 && kLpt <= 16, "row must span 4..16 lanes");
-};
-
-template <int D, bool FP8>
-struct TileRegs {
-  using Geo = Geometry<D, FP8>;
-  u32x4 k[Geo::kNi];
-  u32x4 v[Geo::kNi];
-  float ks, vs;
-  int rows;
-};
-
-template <int D, bool FP8, int NW>
-__device__ __forceinline__ void load_tile(TileRegs<D, FP8>& t, const DecodeArgs& a, const TileWalk<NW>& walk,
-                                          int k, const Unit& u, int lane_off) {
-  using Geo = Geometry<D, FP8>;
-  size_t base;
-  t.rows = tile_base<Geo::kTile, NW>(a, walk, k, u, base);
-  const int nbytes = t.rows * Geo::kRow;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_pool + base, nbytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_pool + base, nbytes);
-  if (a.cached_kv) {
-#pragma unroll
-    for (int i = 0; i < Geo::kNi; ++i) t.k[i] = buffer_load16(rk, lane_off + i * Geo::kTpi * Geo::kRow);
-#pragma unroll
-    for (int i = 0; i < Geo::kNi; ++i) t.v[i] = buffer_load16(rv, lane_off + i * Geo::kTpi * Geo::kRow);
-  } else {
-#pragma unroll
-    for (int i = 0; i < Geo::kNi; ++i) t.k[i] = buffer_load16_kv(rk, lane_off + i * Geo::kTpi * Geo::kRow);
-#pragma unroll
-    for (int i = 0; i < Geo::kNi; ++i) t.v[i] = buffer_load16_kv(rv, lane_off + i * Geo::kTpi * Geo::kRow);
-  }
-  t.ks = t.vs = 1.0f;
-  if constexpr (FP8) {
-    if (t.rows > 0) {
-      const size_t s = base / Geo::kTile;
-      t.ks = a.k_scale[s];
-      t.vs = a.v_scale[s];
-    }
-  }
-}
-
-template <int D, bool FP8>
-__device__ __forceinline__ float lane_dot(const u32x4& kw, const half2_t* qh) {
-  float s = 0.0f;
-  if constexpr (FP8) {
-    const uint32_t w[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      s = __builtin_amdgcn_fdot2(e4m3x2_to_half2<false>(w[k]), qh[2 * k], s, false);
-      s = __builtin_amdgcn_fdot2(e4m3x2_to_half2<true>(w[k]), qh[2 * k + 1], s, false);
-    }
-  } else {
-    s = __builtin_amdgcn_fdot2(as_half2(kw.x), qh[0], s, false);
-    s = __builtin_amdgcn_fdot2(as_half2(kw.y), qh[1], s, false);
-    s = __builtin_amdgcn_fdot2(as_half2(kw.z), qh[2], s, false);
-    s = __builtin_amdgcn_fdot2(as_half2(kw.w), qh[3], s, false);
-  }
-  return s;
-}
-
-template <bool FP8>
-__device__ __forceinline__ void lane_values(const u32x4& vw, float* out) {
-  const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
-  if constexpr (FP8) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float2_t lo = e4m3x2_to_float2<false>(w[k]);
-      const float2_t hi = e4m3x2_to_float2<true>(w[k]);
-      out[4 * k + 0] = lo.x;
-      out[4 * k + 1] = lo.y;
-      out[4 * k + 2] = hi.x;
-      out[4 * k + 3] = hi.y;
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const half2_t h = as_half2(w[k]);
-      out[2 * k + 0] = float(h.x);
-      out[2 * k + 1] = float(h.y);
-    }
-  }
-}
-
-template <int D, int G, bool FP8>
-struct VState {
-  static constexpr int EPL = Geometry<D, FP8>::kEpl;
-  float m[G], l[G], acc[G][EPL];
-};
-
-template <int D, int G, bool FP8>
-__device__ __forceinline__ void valu_tile(VState<D, G, FP8>& st, const TileRegs<D, FP8>& t,
-                                          const half2_t (*qv)[Geometry<D, FP8>::kEpl / 2],
-                                          float scale_log2, int r) {
-  using Geo = Geometry<D, FP8>;
-  constexpr int LPT = Geo::kLpt, TPI = Geo::kTpi, NI = Geo::kNi, EPL = Geo::kEpl;
-  float s[NI][G];  // raw logits of this lane group's rows
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const bool valid = (i * TPI + r) < t.rows;
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float d = group_sum<LPT>(lane_dot<D, FP8>(t.k[i], qv[j]));
-      s[i][j] = valid ? d : -INFINITY;
-    }
-  }
-  float vals[NI][EPL];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) lane_values<FP8>(t.v[i], vals[i]);
-  const float cs = scale_log2 * t.ks;
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float tmax = s[0][j];
-#pragma unroll
-    for (int i = 1; i < NI; ++i) tmax = fmaxf(tmax, s[i][j]);
-    const float mn = fmaxf(st.m[j], tmax * cs);
-    const float alpha = fast_exp2(st.m[j] - mn);
-    st.m[j] = mn;
-    st.l[j] *= alpha;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) st.acc[j][e] *= alpha;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const float pij = fast_exp2(fmaf(s[i][j], cs, -mn));
-      st.l[j] += pij;
-      const float pv = pij * t.vs;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) st.acc[j][e] = fmaf(pv, vals[i][e], st.acc[j][e]);
-    }
-  }
-}
-
-template <int D, int G, bool FP8, int NW>
-__global__ PKV_DECODE_VALU_BOUNDS(NW) void decode_valu_kernel(DecodeArgs a) {
-  using Geo = Geometry<D, FP8>;
-  constexpr int LPT = Geo::kLpt, EPL = Geo::kEpl;
-  const Unit u = decode_unit(a);
-  if (u.empty) return;  // whole workgroup
-
-  const int lane = threadIdx.x & (kWave - 1);
-  // wave index as a scalar: keeps the tile walk, block ids and buffer
-  // resources in SGPRs
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int r = lane / LPT;
-  const int c = lane % LPT;
-
-  half2_t qv[G][EPL / 2];  // q slice of every head: elements [c*EPL, c*EPL + EPL)
-  {
-    const _Float16* qb = static_cast<const _Float16*>(a.q) + (size_t(u.b) * a.Hq + u.kvh * G) * D + c * EPL;
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-#pragma unroll
-      for (int k = 0; k < EPL / 8; ++k) {
-        const u32x4 t = *reinterpret_cast<const u32x4*>(qb + j * D + k * 8);
-        qv[j][4 * k + 0] = as_half2(t.x);
-        qv[j][4 * k + 1] = as_half2(t.y);
-        qv[j][4 * k + 2] = as_half2(t.z);
-        qv[j][4 * k + 3] = as_half2(t.w);
-      }
-    }
-  }
-
-  VState<D, G, FP8> st;
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    st.m[j] = -FLT_MAX;
-    st.l[j] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) st.acc[j][e] = 0.0f;
-  }
-
-  TileWalk<NW> walk;
-  walk.init(a.block_tables + size_t(u.b) * a.MBS, u, w);
-  const int lane_off = r * Geo::kRow + c * 16;
-  TileRegs<D, FP8> ta, tb;
-  for (int c0 = 0; c0 < walk.count; c0 += kWave) {
-    walk.fill(c0);
-    load_tile<D, FP8, NW>(ta, a, walk, c0, u, lane_off);
-    for (int k = c0; k < walk.end;) {
-      load_tile<D, FP8, NW>(tb, a, walk, k + 1, u, lane_off);
-      issue_fence();
-      valu_tile<D, G, FP8>(st, ta, qv, a.scale_log2, r);
-      if (++k >= walk.end) break;
-      load_tile<D, FP8, NW>(ta, a, walk, k + 1, u, lane_off);
-      issue_fence();
-      valu_tile<D, G, FP8>(st, tb, qv, a.scale_log2, r);
-      ++k;
-    }
-  }
-
-  // merge the row groups of the wave (lanes with the same column c)
-#pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float mo = __shfl_xor(st.m[j], off);
-      const float lo = __shfl_xor(st.l[j], off);
-      const float mn = fmaxf(st.m[j], mo);
-      const float fa = fast_exp2(st.m[j] - mn);
-      const float fb = fast_exp2(mo - mn);
-      st.l[j] = st.l[j] * fa + lo * fb;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) st.acc[j][e] = st.acc[j][e] * fa + __shfl_xor(st.acc[j][e], off) * fb;
-      st.m[j] = mn;
-    }
-  }
-
-  __shared__ float s_acc[NW][G][D];
-  __shared__ float s_m[NW][G];
-  __shared__ float s_l[NW][G];
-  if (r == 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[w][j][c * EPL + e] = st.acc[j][e];
-      if (c == 0) {
-        s_m[w][j] = st.m[j];
-        s_l[w][j] = st.l[j];
-      }
-    }
-  }
-  __syncthreads();
-  combine_and_store<D, G, NW>(a, u, s_acc, s_m, s_l, a.partition_size == 0);
-}
-
-// ---------------------------------------------------------------------------
 // Dispatch.
 
 constexpr int kWavesPerGroup = PKV_DECODE_WAVES;
@@ -669,13 +417,7 @@ hipError_t launch_mfma(const DecodeArgs& a, int B, hipStream_t stream) {
 }
 
 template <int D, int G, bool FP8>
-hipError_t launch_typed(const DecodeArgs& a, int B, DecodeEngine engine, hipStream_t stream) {
-  if (engine == DecodeEngine::kValu) {
-    const unsigned units = unsigned(int64_t(B) * a.Hkv * a.max_partitions);
-    hipLaunchKernelGGL((decode_valu_kernel<D, G, FP8, kWavesPerGroup>), dim3(units),
-                       dim3(kWavesPerGroup * kWave), 0, stream, a);
-    return hipGetLastError();
-  }
+hipError_t launch_typed(const DecodeArgs& a, int B, hipStream_t stream) {
   return launch_mfma<D, G, FP8, kModeAttend>(a, B, stream);
 }
 
@@ -708,10 +450,9 @@ hipError_t by_group(int group, F&& f) {
 }
 
 template <int D, bool FP8>
-hipError_t launch_group(const DecodeArgs& a, int B, int group, DecodeEngine engine,
-                        hipStream_t stream) {
+hipError_t launch_group(const DecodeArgs& a, int B, int group, hipStream_t stream) {
   return by_group<D, FP8>(group, [&](auto gc) {
-    return launch_typed<D, decltype(gc)::value, FP8>(a, B, engine, stream);
+    return launch_typed<D, decltype(gc)::value, FP8>(a, B, stream);
   });
 }
 
@@ -725,11 +466,11 @@ hipError_t launch_step_group(const DecodeArgs& a, int B, int group, int mode, hi
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, int group, bool fp8,
-                         DecodeEngine engine, hipStream_t stream) {
-  if (D == 128) return fp8 ? launch_group<128, true>(a, B, group, engine, stream)
-                           : launch_group<128, false>(a, B, group, engine, stream);
-  if (D == 64) return fp8 ? launch_group<64, true>(a, B, group, engine, stream)
-                          : launch_group<64, false>(a, B, group, engine, stream);
+                         hipStream_t stream) {
+  if (D == 128) return fp8 ? launch_group<128, true>(a, B, group, stream)
+                           : launch_group<128, false>(a, B, group, stream);
+  if (D == 64) return fp8 ? launch_group<64, true>(a, B, group, stream)
+                          : launch_group<64, false>(a, B, group, stream);
   return hipErrorInvalidValue;
 }
 

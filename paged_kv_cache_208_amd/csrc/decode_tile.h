@@ -173,12 +173,18 @@ __device__ __forceinline__ uint32_t word(const typename Words<W>::T& v, int k) {
   else return v[k];
 }
 
+// E4M3 scales of a tile: the K scale multiplies the logits (fp32); the V
+// scale is split in two factors so that neither fp16 operand of the P.V
+// product leaves the normal range whatever the data's magnitude: its
+// power-of-two part is applied exactly in the conversion of the V codes,
+// and its mantissa vm in [1, 2) multiplies the softmax weights (in [0, 1])
+// before they are rounded to fp16.
 template <int D, bool FP8>
 struct MTile {
   using Geo = MfmaGeo<D, FP8>;
   u32x4 k[Geo::kKLoads];
   typename Words<Geo::kVWords>::T v[4];
-  float ks, vs;
+  float ks, vs, vm;
   int rows;  // rows [lo, rows) take part; the others are masked out
   int lo;
 };
@@ -211,12 +217,13 @@ __device__ __forceinline__ void load_mtile_at(MTile<D, FP8>& t, const DecodeArgs
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_pool + base, nbytes);
   if (cached) mtile_loads<D, FP8, 0>(t, rk, rv, k_off, v_off);
   else mtile_loads<D, FP8, kKvAux>(t, rk, rv, k_off, v_off);
-  t.ks = t.vs = 1.0f;
+  t.ks = t.vs = t.vm = 1.0f;
   if constexpr (FP8) {
     if (rows > 0) {
       const size_t s = (base / Geo::kTile) >> a.bs_shift;  // == block id * Hkv + kv head
       t.ks = load_uniform_f32(a.k_scale + s);
       t.vs = load_uniform_f32(a.v_scale + s);
+      t.vm = scale_mantissa(t.vs);
     }
   }
 }
@@ -275,7 +282,7 @@ __device__ __forceinline__ half4_t v_operand(const MTile<D, FP8>& t, int i) {
     const uint32_t p01 = __builtin_amdgcn_perm(x1, x0, sel);
     const uint32_t p23 = __builtin_amdgcn_perm(x3, x2, sel);
     const uint32_t w = __builtin_amdgcn_perm(p23, p01, i % 2 ? 0x07060302u : 0x05040100u);
-    const half2_t a = e4m3x2_to_half2<false>(w), c = e4m3x2_to_half2<true>(w);
+    const half2_t a = e4m3x2_to_half2_pow2<false>(w, t.vs), c = e4m3x2_to_half2_pow2<true>(w, t.vs);
     return half4_t{a.x, a.y, c.x, c.y};
   }
 }
@@ -296,16 +303,19 @@ __device__ __forceinline__ void mfma_tile(MState<D, FP8>& st, const MTile<D, FP8
 #pragma unroll
   for (int c = 0; c < Geo::kQK; ++c)
     s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<D, FP8>(t, c), qop[c], s, 0, 0, 0);
+  // logits in log2 units; rows outside [lo, min(rows, col_hi)) are masked
+  // after the scaling, so a zero E4M3 K scale (a block whose rows are all
+  // zero) gives zero logits, never -inf * 0
   const float cs = scale_log2 * t.ks;
   float tm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    s[r] = (4 * g + r) < min(t.rows, col_hi) && (4 * g + r) >= t.lo ? s[r] : -INFINITY;
+    s[r] = (4 * g + r) < min(t.rows, col_hi) && (4 * g + r) >= t.lo ? s[r] * cs : -INFINITY;
     tm = fmaxf(tm, s[r]);
   }
   // the head's 16 tokens sit in lanes n16, n16+16, n16+32, n16+48
   tm = group4_max(tm);
-  const float mn = fmaxf(st.m, tm * cs);
+  const float mn = fmaxf(st.m, tm);
   const float alpha = fast_exp2(st.m - mn);
   st.m = mn;
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // skip the rescale when no max moved
@@ -316,11 +326,12 @@ __device__ __forceinline__ void mfma_tile(MState<D, FP8>& st, const MTile<D, FP8
   float p[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    p[r] = fast_exp2(fmaf(s[r], cs, -mn));
+    p[r] = fast_exp2(s[r] - mn);
     st.l += p[r];
   }
-  const half4_t pv = {(_Float16)(p[0] * t.vs), (_Float16)(p[1] * t.vs), (_Float16)(p[2] * t.vs),
-                      (_Float16)(p[3] * t.vs)};
+  half4_t pv;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pv[r] = (_Float16)(FP8 ? p[r] * t.vm : p[r]);
 #pragma unroll
   for (int i = 0; i < Geo::kPV; ++i)
     st.acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v_operand<D, FP8>(t, i), pv, st.acc[i], 0, 0, 0);

@@ -66,9 +66,26 @@ __device__ __forceinline__ half2_t e4m3x2_to_half2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
 }
 
+// The same conversion multiplied by the power-of-two part of `scale`: the
+// gfx950 instruction applies 2^floor(log2 scale) (the exponent of the fp32
+// scale, as for MX block scales; checked on MI355X for every code and for
+// scales 0, 2^-20 .. 2^10 and non-powers of two), so the product is the
+// exact value code * 2^e rounded once to fp16 (exact unless it is an fp16
+// subnormal).
+template <bool HI>
+__device__ __forceinline__ half2_t e4m3x2_to_half2_pow2(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, scale, HI);
+}
+
 template <bool HI>
 __device__ __forceinline__ float2_t e4m3x2_to_float2(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
+// scale / 2^floor(log2 scale), in [1, 2) for a normal positive scale (1.0 for
+// zero): the part of the scale that the conversion above leaves out.
+__device__ __forceinline__ float scale_mantissa(float scale) {
+  return __uint_as_float((__float_as_uint(scale) & 0x007FFFFFu) | 0x3F800000u);
 }
 
 }  // namespace pkv

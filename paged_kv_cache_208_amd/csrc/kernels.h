@@ -92,12 +92,9 @@ struct CopyArgs {
   int Hkv;
 };
 
-// Tile engine of the decode kernel (same result, different instruction mix).
-enum class DecodeEngine { kMfma, kValu };
-
 // Launchers return the hipError_t of the launch.
 hipError_t launch_decode(const DecodeArgs& a, int B, int D, int group, bool fp8,
-                         DecodeEngine engine, hipStream_t stream);
+                         hipStream_t stream);
 hipError_t launch_decode_step(const DecodeArgs& a, int B, int D, int group, bool fp8, int mode,
                               hipStream_t stream);
 // cols = (Hq / Hkv) * nq, the used columns of the 16-wide products (1..16)

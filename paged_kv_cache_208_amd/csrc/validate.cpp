@@ -144,13 +144,14 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
   if (!supported_block_size(BS)) return PKV_EUNSUPPORTED;
   if (BS != pkv::kBlockSize && partition_size != 0) return PKV_EUNSUPPORTED;
   const int tiles = BS / pkv::kBlockSize;
-  // the attention part is checked as paged_attn_decode checks partitioned work
-  // (partition_size 0 here means a balanced split, which needs the same workspace)
-  const int ps_check = partition_size == 0 ? pkv::kBlockSize : partition_size;
+  // the attention part is checked as paged_attn_decode checks it: fixed
+  // partitions as partitioned work (one workgroup per partition), the
+  // balanced split as a single pass (its grid does not grow with the
+  // context; its workspace is checked below)
   int st = pkv_validate_decode(out, q, k_pool, v_pool, k_scale, v_scale, block_tables,
                                context_lens, B, Hq, Hkv, D, pkv::kBlockSize, MBS * tiles,
-                               NB * tiles, scale, kv_dtype, ps_check, part_out, part_max, part_sum,
-                               partition_size == 0 ? MBS * tiles : max_partitions);
+                               NB * tiles, scale, kv_dtype, partition_size, part_out, part_max,
+                               part_sum, partition_size == 0 ? 1 : max_partitions);
   if (st != PKV_OK) return st;
   if (window < 0) return PKV_EINVAL;
   if (window > 0 && partition_size != 0) return PKV_EUNSUPPORTED;  // balanced split only
@@ -167,6 +168,9 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
   if (!counters || !aligned(counters, 4)) return PKV_EINVAL;
   if (partition_size == 0) {
     // balanced split: between 3 and 64 pieces per sequence
+    if (!part_out || !part_max || !part_sum) return PKV_EINVAL;
+    if (!aligned(part_out, 16) || !aligned(part_max, 4) || !aligned(part_sum, 4))
+      return PKV_EINVAL;
     if (max_partitions < 3) return PKV_EINVAL;
     if (max_partitions > pkv::kMaxStepPartitions) return PKV_EUNSUPPORTED;
   } else {

@@ -24,7 +24,8 @@ TornadoVM batched decode", Serving / scheduling):
 Draw order per config (numpy default_rng(208000 + k) for config ck):
 context_lens (and prefix tails) -> block permutation -> Q -> K -> V ->
 (fused config) gamma_q, gamma_k, k_new, v_new.  Values are float32 N(0, 1)
-rounded to fp16; gamma ~ N(1, 0.1) float32.
+rounded to fp16 (pool K/V: N(0, 1) times kv_sigma, 1 unless a test asks
+for another data scale); gamma ~ N(1, 0.1) float32.
 """
 
 from __future__ import annotations
@@ -61,6 +62,7 @@ class DecodeConfig:
     seed: int = 208000
     description: str = ""
     block_size: int = BLOCK_SIZE     # tokens per physical block (16 or 32)
+    kv_sigma: float = 1.0            # K/V values are N(0, kv_sigma^2) before rounding
 
     @property
     def group(self) -> int:
@@ -108,8 +110,11 @@ CONFIGS = {
 }
 
 
-def _normal_f16(rng, shape) -> np.ndarray:
-    return rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+def _normal_f16(rng, shape, sigma=1.0) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if sigma != 1.0:
+        x = x * np.float32(sigma)
+    return x.astype(np.float16)
 
 
 def _quantise_e4m3(tiles_f16: np.ndarray):
@@ -179,7 +184,7 @@ def generate(cfg: DecodeConfig, *, seed: int | None = None) -> dict:
             sc = None
         for lo in range(0, len(used_ids), _CHUNK_BLOCKS):
             ids = used_ids[lo:lo + _CHUNK_BLOCKS]
-            vals = _normal_f16(rng, (len(ids), Hkv, BS, D))
+            vals = _normal_f16(rng, (len(ids), Hkv, BS, D), cfg.kv_sigma)
             if fp8:
                 codes, s = _quantise_e4m3(vals)
                 pool[ids] = codes

@@ -228,6 +228,13 @@ def _step_args(**kw):
     (dict(max_partitions=1), -1),
     (dict(partition_size=16, MBS=65, max_partitions=65), -2),
     (dict(partition_size=16, MBS=64, max_partitions=64), 0),
+    # the balanced split's grid is fixed: a long-context batch is accepted
+    # (B = 512, 8 kv heads, 128K-token tables) ...
+    (dict(partition_size=0, max_partitions=16, B=512, Hq=64, Hkv=8, MBS=8192, NB=10 ** 6), 0),
+    # ... which fixed partitions of 16 tokens could not launch
+    (dict(partition_size=16, max_partitions=8192, B=512, Hq=64, Hkv=8, MBS=8192, NB=10 ** 6), -2),
+    (dict(partition_size=0, max_partitions=16, part_max=None), -1),
+    (dict(partition_size=0, max_partitions=16, part_sum=A + 2), -1),
 ])
 def test_step_validation_codes(lib, kw, code):
     assert lib.pkv_validate_step(*_step_args(**kw).values()) == code
