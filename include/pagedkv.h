@@ -3,7 +3,8 @@
  *
  * C ABI of libpagedkv.so.  Every entry point takes plain pointers and sizes;
  * no allocation, no synchronisation and no state is kept by the library
- * (thread-safe).  Device pointers are caller-owned HIP device memory; work
+ * (thread-safe), except for the per-GPU scratch of paged_decode_step_static
+ * (see there).  Device pointers are caller-owned HIP device memory; work
  * is enqueued on `stream` (a hipStream_t passed as void*, NULL = the null
  * stream) and the call returns without waiting for it.
  *
@@ -62,7 +63,9 @@ typedef enum {
   PKV_OK = 0,
   PKV_EINVAL = -1,       /* null/misaligned pointer, inconsistent sizes      */
   PKV_EUNSUPPORTED = -2, /* valid but not built: head_dim, group, block size */
-  PKV_ELAUNCH = -3       /* the HIP launch itself failed                     */
+  PKV_ELAUNCH = -3,      /* the HIP launch itself failed                     */
+  PKV_ENOSPACE = -4      /* paged_decode_step_static: the batch does not fit
+                            the library's static scratch                     */
 } pkv_status;
 
 typedef enum { PKV_KV_F16 = 0, PKV_KV_E4M3 = 1 } pkv_kv_dtype;
@@ -267,6 +270,45 @@ int paged_kv_append_e4m3(const void* k_new, const void* v_new, void* k_pool, voi
 int paged_kv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                          const int32_t* src, const int32_t* dst, int n, int Hkv, int D, int BS,
                          int64_t NB, int kv_dtype, void* stream);
+
+/*
+ * paged_decode_step_static - paged_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same step, with the split-context
+ * partials and arrival counters kept in a scratch array the library holds
+ * in each GPU's memory (32 MiB per GPU, taken when the library's code is
+ * loaded on that GPU and held until the process ends) instead of a
+ * caller-owned workspace.  Arguments are those of paged_decode_step without
+ * part_out / part_max / part_sum / counters / max_partitions; the caller
+ * still passes every input and output.  Nothing is allocated or freed: no
+ * hipMalloc, no allocating library routine.
+ *
+ * Limits: B * Hkv <= 262144, and the partials of every output row must fit
+ * the remaining 31 MiB; the pieces per sequence are
+ * paged_decode_step_static_partitions(...) (balanced split: 16, or fewer for
+ * large batches, at least 3; fixed partitions: ceil(MBS * BS /
+ * partition_size)).  A batch beyond that returns PKV_ENOSPACE and enqueues
+ * nothing.  The first call on each GPU also enqueues, on its stream and
+ * ahead of its step, one small kernel that zeroes the counters (every step
+ * leaves them at zero).
+ *
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on
+ * one GPU (other streams, other host threads) race and give undefined
+ * results.  Results equal paged_decode_step's with max_partitions set to
+ * paged_decode_step_static_partitions(...).
+ */
+int paged_decode_step_static(void* out, void* q, const void* k_new, const void* v_new,
+                             void* k_pool, void* v_pool, const float* k_scale,
+                             const float* v_scale, const int32_t* block_tables,
+                             const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
+                             int MBS, int64_t NB, float scale, int kv_dtype, int partition_size,
+                             int window, int n_query, const float* gamma_q,
+                             const float* gamma_k, float eps, float rope_theta, void* stream);
+
+/* Pieces per sequence paged_decode_step_static uses for these sizes (>= 1),
+   or PKV_EINVAL / PKV_ENOSPACE.  Host only. */
+int paged_decode_step_static_partitions(int B, int Hq, int Hkv, int D, int BS, int MBS,
+                                        int n_query, int partition_size);
 
 /* Bytes of part_out + part_max + part_sum for the given sizes (0 on overflow). */
 size_t paged_attn_workspace_size(int B, int Hq, int D, int max_partitions);

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # PAGEDKV_LIB points at another build of the same library (e.g. a tuning variant)
 LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(_HERE, "libpagedkv.so")
 
-PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH = 0, -1, -2, -3
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH, PKV_ENOSPACE = 0, -1, -2, -3, -4
 PKV_KV_F16, PKV_KV_E4M3 = 0, 1
 PKV_KV_SHARED_BLOCKS = 0x100  # cache-policy hint OR-ed into kv_dtype
 BLOCK_SIZE = 16
@@ -38,6 +38,9 @@ _SIGNATURES = {
     "paged_attn_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                _I64, _F, _I, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I, _P]),
+    "paged_decode_step_static": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                      _I, _I64, _F, _I, _I, _I, _I, _P, _P, _F, _F, _P]),
+    "paged_decode_step_static_partitions": (_I, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "paged_kv_copy_blocks": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I, _P]),
     "paged_kv_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P]),
     "paged_attn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
@@ -372,3 +375,54 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                                  _ptr(gamma_k), float(eps), float(rope_theta), _ptr(po), _ptr(pm),
                                  _ptr(ps), _ptr(ctr), P, _stream(stream))
     _raise("paged_decode_step", st)
+
+
+def static_step_partitions(B, Hq, Hkv, D, BS, MBS, n_query=1, partition_size=0) -> int:
+    """Pieces per sequence paged_decode_step_static uses (raises if the batch
+    does not fit its static scratch)."""
+    P = lib().paged_decode_step_static_partitions(B, Hq, Hkv, D, BS, MBS, n_query,
+                                                   partition_size)
+    _raise("paged_decode_step_static_partitions", min(P, 0))
+    return P
+
+
+def paged_decode_step_static(out, q, k_pool, v_pool, block_tables, context_lens, scale, *,
+                             k_new=None, v_new=None, k_scale=None, v_scale=None,
+                             partition_size=0, window=0, gamma_q=None, gamma_k=None, eps=1e-6,
+                             rope_theta=1e6, shared_blocks=False, stream=None):
+    """paged_decode_step with the library's static scratch instead of a
+    workspace: allocates nothing.  Calls on one GPU must not overlap."""
+    nq = 1
+    if q.dim() == 4:
+        nq = q.shape[1]
+        q3, out3 = q.reshape(q.shape[0], -1, q.shape[3]), out.reshape(out.shape[0], -1, out.shape[3])
+    else:
+        q3, out3 = q, out
+    _check(out3, "out", torch.float16, 3)
+    _check(q3, "q", torch.float16, 3)
+    kv = _kv_dtype(k_pool) | (PKV_KV_SHARED_BLOCKS if shared_blocks else 0)
+    _check(k_pool, "k_pool", k_pool.dtype, 4)
+    _check(v_pool, "v_pool", k_pool.dtype, 4)
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(context_lens, "context_lens", torch.int32, 1)
+    B, HqN, D = q3.shape
+    Hq = HqN // nq
+    NB, Hkv, BS, d2 = k_pool.shape
+    if d2 != D or v_pool.shape != k_pool.shape or tuple(out3.shape) != (B, HqN, D):
+        raise ValueError("q / out / pool shapes disagree")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables / context_lens must have B rows")
+    if k_new is not None:
+        want = (B, Hkv, D) if nq == 1 else (B, nq, Hkv, D)
+        _check(k_new, "k_new", torch.float16, len(want))
+        _check(v_new, "v_new", torch.float16, len(want))
+        if tuple(k_new.shape) != want or tuple(v_new.shape) != want:
+            raise ValueError(f"k_new / v_new must be {list(want)}")
+    st = lib().paged_decode_step_static(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                        _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                        _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, BS,
+                                        block_tables.shape[1], NB, float(scale), kv,
+                                        int(partition_size), int(window), nq, _ptr(gamma_q),
+                                        _ptr(gamma_k), float(eps), float(rope_theta),
+                                        _stream(stream))
+    _raise("paged_decode_step_static", st)

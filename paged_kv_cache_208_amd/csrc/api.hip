@@ -6,10 +6,65 @@
 #include "device.h"
 #include "shape_limits.h"
 
+#include <mutex>
+
 
 namespace {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
+
+// ---------------------------------------------------------------------------
+// Static scratch of paged_decode_step_static: the arrival counters (first
+// kScratchCounterBytes, zero between calls) and then the partials.  One copy
+// per GPU, held until the process ends.  The host never uses the array's
+// name as an address (in host code it is only a stand-in for the symbol):
+// its device address is looked up once per device and kept.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr size_t kScratchCounterBytes = size_t(1) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct DeviceScratch {
+  std::once_flag addr_once, fill_once;
+  unsigned char* ptr = nullptr;
+  hipError_t addr_err = hipSuccess, fill_err = hipSuccess;
+};
+DeviceScratch g_scratch[kMaxDevices];
+
+__global__ void fill_zero_u32(uint32_t* p, int n) {
+  const int i = int(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
+// This device's scratch: its device address, looked up once per device with
+// the device current (nothing is enqueued).
+int scratch_address(int* dev_out, unsigned char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ELAUNCH;
+  DeviceScratch& d = g_scratch[dev];
+  std::call_once(d.addr_once, [&] {
+    void* p = nullptr;
+    d.addr_err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (d.addr_err == hipSuccess) d.ptr = static_cast<unsigned char*>(p);
+  });
+  if (d.addr_err != hipSuccess || d.ptr == nullptr) return PKV_ELAUNCH;
+  *dev_out = dev;
+  *out = d.ptr;
+  return PKV_OK;
+}
+
+// The first call on a device zeroes the counters with a fill kernel on its
+// stream (ahead of its own step kernel); every step leaves them at zero.
+int scratch_fill_once(int dev, unsigned char* base, hipStream_t stream) {
+  DeviceScratch& d = g_scratch[dev];
+  std::call_once(d.fill_once, [&] {
+    const int n = int(kScratchCounterBytes / sizeof(uint32_t));
+    hipLaunchKernelGGL(fill_zero_u32, dim3((n + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t*>(base), n);
+    d.fill_err = hipGetLastError();
+  });
+  return d.fill_err == hipSuccess ? PKV_OK : PKV_ELAUNCH;
+}
 
 }  // namespace
 
@@ -175,4 +230,59 @@ extern "C" int pkv_stream_read(const void* buf, int64_t bytes, uint32_t* sink, v
     cus = 256;
   return launch_status(pkv::launch_stream_read(buf, bytes, sink, cus,
                                                static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int paged_decode_step_static_partitions(int B, int Hq, int Hkv, int D, int BS, int MBS,
+                                                   int n_query, int partition_size) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || MBS <= 0 || n_query < 1 ||
+      partition_size < 0)
+    return PKV_EINVAL;
+  if (int64_t(B) * Hkv * int64_t(sizeof(uint32_t)) > int64_t(kScratchCounterBytes))
+    return PKV_ENOSPACE;
+  // bytes of one partial slot of every output row
+  const int64_t per_slot = int64_t(B) * Hq * n_query * (int64_t(D) + 2) * int64_t(sizeof(float));
+  const int64_t room = int64_t(kScratchBytes - kScratchCounterBytes);
+  int P;
+  if (partition_size > 0) {
+    P = int((int64_t(MBS) * BS + partition_size - 1) / partition_size);
+  } else {
+    const int64_t fit = per_slot > 0 ? room / per_slot : pkv::kStaticStepPartitions;
+    P = int(fit < pkv::kStaticStepPartitions ? fit : pkv::kStaticStepPartitions);
+    if (P < 3) return PKV_ENOSPACE;
+  }
+  if (int64_t(P) * per_slot > room) return PKV_ENOSPACE;
+  return P;
+}
+
+extern "C" int paged_decode_step_static(void* out, void* q, const void* k_new, const void* v_new,
+                                        void* k_pool, void* v_pool, const float* k_scale,
+                                        const float* v_scale, const int32_t* block_tables,
+                                        const int32_t* context_lens, int B, int Hq, int Hkv, int D,
+                                        int BS, int MBS, int64_t NB, float scale, int kv_dtype,
+                                        int partition_size, int window, int n_query,
+                                        const float* gamma_q, const float* gamma_k, float eps,
+                                        float rope_theta, void* stream) {
+  const int P = paged_decode_step_static_partitions(B, Hq, Hkv, D, BS, MBS, n_query,
+                                                    partition_size);
+  if (P < 0) return P;
+  int dev = 0;
+  unsigned char* base = nullptr;
+  const int sa = scratch_address(&dev, &base);
+  if (sa != PKV_OK) return sa;
+  const size_t rows = size_t(B) * Hq * n_query * P;
+  uint32_t* counters = reinterpret_cast<uint32_t*>(base);
+  float* part_out = reinterpret_cast<float*>(base + kScratchCounterBytes);
+  float* part_max = part_out + rows * D;
+  float* part_sum = part_max + rows;
+  const int st = pkv_validate_step(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
+                                   block_tables, context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale,
+                                   kv_dtype, partition_size, window, n_query, gamma_q, gamma_k,
+                                   eps, rope_theta, part_out, part_max, part_sum, counters, P);
+  if (st != PKV_OK || B == 0) return st;
+  const int sf = scratch_fill_once(dev, base, static_cast<hipStream_t>(stream));
+  if (sf != PKV_OK) return sf;
+  return paged_decode_step(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_tables,
+                           context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale, kv_dtype,
+                           partition_size, window, n_query, gamma_q, gamma_k, eps, rope_theta,
+                           part_out, part_max, part_sum, counters, P, stream);
 }

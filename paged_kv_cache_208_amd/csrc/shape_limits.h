@@ -11,4 +11,5 @@ constexpr int64_t kMaxContext = int64_t(1) << 24;   // MBS * BS
 constexpr int64_t kMaxGrid = (int64_t(1) << 24) - 1;  // workgroups per launch (x <= 2^32 / 256)
 constexpr int64_t kMaxAppendRows = int64_t(1) << 24;
 constexpr int kMaxStepPartitions = 64;     // partitions one step combines in-kernel
+constexpr int kStaticStepPartitions = 16;  // pieces per sequence of the static-scratch step
 }  // namespace pkv

@@ -28,6 +28,7 @@ extern "C" const char* pkv_strerror(int status) {
     case PKV_EINVAL: return "invalid argument (null or misaligned pointer, or inconsistent sizes)";
     case PKV_EUNSUPPORTED: return "unsupported configuration (head_dim, GQA group, block size or partition size)";
     case PKV_ELAUNCH: return "HIP kernel launch failed";
+    case PKV_ENOSPACE: return "the batch does not fit the library's static scratch (32 MiB per GPU)";
     default: return "unknown pkv status";
   }
 }

@@ -50,7 +50,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_strerror_and_workspace(lib):
     assert _lib.strerror(0) == "ok"
-    for code in (-1, -2, -3, 7):
+    assert "static scratch" in _lib.strerror(-4)
+    for code in (-1, -2, -3, -4, 7):
         assert isinstance(_lib.strerror(code), str)
     assert _lib.workspace_size(2, 4, 128, 3) == 2 * 4 * 3 * 130 * 4
     assert _lib.workspace_size(-1, 4, 128, 3) == 0
@@ -297,3 +298,26 @@ def test_append_e4m3_validation_codes(lib, kw, code):
 ])
 def test_stream_read_rejects_bad_arguments_before_any_launch(lib, buf, nbytes, sink):
     assert lib.pkv_stream_read(buf, nbytes, sink, None) == -1
+
+
+def test_static_step_partitions(lib):
+    """The static-scratch step's pieces per sequence: 16 while the partials
+    fit 31 MiB, fewer for large batches, never fewer than 3; fixed
+    partitions need ceil(MBS * BS / partition_size) slots."""
+    f = lib.paged_decode_step_static_partitions
+    assert f(32, 32, 8, 128, 16, 256, 1, 0) == 16               # LLaMA-3-8B-shaped batch
+    assert f(256, 32, 8, 128, 16, 512, 1, 0) == 7               # Qwen3-8B-shaped batch
+    assert f(32, 32, 8, 128, 16, 256, 1, 512) == 8              # fixed 512-token partitions
+    assert f(4096, 64, 8, 128, 16, 8, 1, 0) == -4               # partials do not fit
+    assert f(40000, 8, 8, 128, 16, 8, 1, 0) == -4               # counters do not fit
+    assert f(-1, 8, 8, 128, 16, 8, 1, 0) == -1
+    per_slot = 256 * 32 * 130 * 4
+    assert 7 * per_slot <= (31 << 20) < 8 * per_slot
+
+
+def test_static_step_rejects_a_batch_beyond_the_scratch(lib):
+    """Rejected on the host, before any HIP call."""
+    a = _step_args(partition_size=0, B=4096, Hq=64, Hkv=8)
+    for k in ("part_out", "part_max", "part_sum", "counters", "max_partitions"):
+        a.pop(k)
+    assert lib.paged_decode_step_static(*a.values(), None) == -4
