@@ -79,28 +79,32 @@ __device__ __forceinline__ int window_start(int L, int W) { return (W > 0 && L >
 __device__ __forceinline__ int first_tile(int L, int W) { return window_start(L, W) / 16; }
 __device__ __forceinline__ int seg_tiles(int L, int W) { return (L + 15) / 16 - first_tile(L, W); }
 
-__device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
-  const int lo = __builtin_amdgcn_readlane(int(uint64_t(v) & 0xffffffffu), lane);
-  const int hi = __builtin_amdgcn_readlane(int(uint64_t(v) >> 32), lane);
-  return int64_t((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo));
+// Quotient of non-negative a / b, with the 32-bit division when both fit
+// (every realistic batch: a 64-bit division is a long software sequence).
+__device__ __forceinline__ int64_t div_nn(int64_t a, int64_t b) {
+  if (((uint64_t(a) | uint64_t(b)) >> 32) == 0) return int64_t(uint32_t(a) / uint32_t(b));
+  return a / b;
 }
 
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int64_t wave_scan(int64_t x) {
+// Inclusive prefix sum over the 64 lanes (tile counts: a chunk of 64
+// sequences holds far fewer than 2^31 tiles).
+__device__ __forceinline__ int wave_scan(int x) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    const int64_t y = __shfl_up(x, off);
+    const int y = __shfl_up(x, off);
     if (lane >= off) x += y;
   }
   return x;
 }
 
 // Tiles of the batch (all kv heads), of one kv head, and the most tiles of
-// one sequence.
+// one sequence; incl0: this lane's inclusive prefix sum over the first
+// chunk of 64 sequences (all of them when B <= 64), which locate() reuses.
 struct Totals {
   int64_t tiles, per_head;
   int max_tiles;
+  int incl0;
 };
 
 // L0: this lane's length in the first chunk of 64 sequences, read once by
@@ -108,32 +112,34 @@ struct Totals {
 __device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B, int L0, int W) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t tot = 0;
-  int mx = 0;
+  int mx = 0, incl0 = 0;
   for (int c = 0; c < B; c += kWave) {
     const int b = c + lane;
     const int T = seg_tiles(c == 0 ? L0 : b < B ? a.context_lens[b] : 0, W);
-    const int64_t incl = wave_scan(int64_t(T));
-    tot += readlane64(incl, kWave - 1);
+    const int incl = wave_scan(T);
+    if (c == 0) incl0 = incl;
+    tot += __builtin_amdgcn_readlane(incl, kWave - 1);
     mx = max(mx, T);
   }
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) mx = max(mx, __shfl_xor(mx, off));
-  return Totals{tot * a.Hkv, tot, __builtin_amdgcn_readfirstlane(mx)};
+  return Totals{tot * a.Hkv, tot, __builtin_amdgcn_readfirstlane(mx), incl0};
 }
 
 // Cursor of flattened tile t (t < total); wh = tiles of one kv head.
 __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, int64_t wh, int L0,
-                                        int W) {
+                                        int incl0, int W) {
   const int lane = threadIdx.x & (kWave - 1);
   Cursor c{};
-  c.kvh = int(t / wh);
+  c.kvh = int(div_nn(t, wh));
   const int64_t r = t - int64_t(c.kvh) * wh;  // position within the head's run
   int64_t carry = 0;
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
     const int L = c0 == 0 ? L0 : b < B ? a.context_lens[b] : 0;
-    const int64_t w = seg_tiles(L, W);
-    const int64_t hi = carry + wave_scan(w);
+    const int w = seg_tiles(L, W);
+    const int incl = c0 == 0 ? incl0 : wave_scan(w);
+    const int64_t hi = carry + incl;
     const int64_t lo = hi - w;
     const uint64_t here = __builtin_amdgcn_ballot_w64(b < B && lo <= r && r < hi);
     if (here) {
@@ -142,11 +148,12 @@ __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, 
       c.L = __builtin_amdgcn_readlane(L, src);
       c.T = seg_tiles(c.L, W);
       c.f = first_tile(c.L, W);
-      c.n = int(r - readlane64(lo, src));
-      c.S = int64_t(c.kvh) * wh + readlane64(lo, src);
+      const int64_t lo_src = carry + __builtin_amdgcn_readlane(incl - w, src);
+      c.n = int(r - lo_src);
+      c.S = int64_t(c.kvh) * wh + lo_src;
       return c;
     }
-    carry = readlane64(hi, kWave - 1);
+    carry += __builtin_amdgcn_readlane(incl, kWave - 1);
   }
   return c;  // not reached for t < total
 }
@@ -176,25 +183,56 @@ __device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B, i
 #endif
 
 // The wave ranges, back to back in the flattened order, in nblk blocks of
-// per = workers / nblk ranges (one block per XCD when the grid allows it):
-// in each block the first nh = per / 2 ranges hold ta tiles, the others tb.
+// per = workers / nblk ranges (one block per XCD when the grid allows it).
 // Wave w (on XCD w % nblk) reads range (w % nblk) * per + w / nblk, so an
 // XCD's waves read one contiguous block, and the first half of the waves (w
-// < workers / 2) get the ta ranges.  With two waves per SIMD the first wave
-// placed on a SIMD is served first when both are ready to issue, and equal
-// shares end far apart; that half then takes the larger share (skew ta : tb,
-// in percent).  Every range is long enough that no sequence is cut into more
-// than P pieces: T tiles span at most (T - 1) / r + 2 ranges of r >= rmin
-// tiles.
+// < workers / 2) read the first nh = per / 2 ranges of each block.  With two
+// waves per SIMD the first wave placed on a SIMD is served first when both
+// are ready to issue, and equal shares end far apart; that half then takes
+// the larger share (skew, in percent of the other half's).
+//
+// Even split (the usual case): block x covers tiles [floor(x W / nblk),
+// floor((x + 1) W / nblk)); its first half of ranges share A = its tiles *
+// skew / (skew + 100), the second half the rest, and n ranges share S tiles
+// as [floor(i S / n), floor((i + 1) S / n)), so no two ranges of a half
+// differ by more than one tile.  Every range must still be long enough that
+// no sequence is cut into more than P pieces (T tiles span at most
+// (T - 1) / r + 2 ranges of r >= rmin tiles); when the shares are shorter
+// than that (small batches) the ranges are rmin tiles each, back to back.
+// a / d for a >= 0, a shift when d = 2^lg (lg >= 0).
+__device__ __forceinline__ int64_t div_by(int64_t a, int64_t d, int lg) {
+  return lg >= 0 ? a >> lg : div_nn(a, d);
+}
+
+__device__ __forceinline__ int log2_if_pow2(int64_t d) {
+  return d > 0 && (d & (d - 1)) == 0 ? int(__builtin_ctzll(uint64_t(d))) : -1;
+}
+
 struct Ranges {
-  int64_t ta, tb, nh, per, blk;
-  __device__ __forceinline__ int64_t start(int64_t r) const {
-    const int64_t x = r / per, i = r - x * per;
-    return x * blk + (i <= nh ? i * ta : nh * ta + (i - nh) * tb);
+  int64_t W;        // tiles in total
+  int64_t nblk, per, nh;
+  int lg_nblk, lg_per, lg_nh, lg_rest;  // log2 of nblk, per, nh, per - nh when powers of two
+  int skew;         // percent
+  bool even;
+  int64_t r;        // range length when !even
+  __device__ __forceinline__ int64_t block_start(int64_t x) const { return div_by(x * W, nblk, lg_nblk); }
+  __device__ __forceinline__ int64_t half_tiles(int64_t S) const {
+    return skew == 100 ? S >> 1 : div_nn(S * skew, skew + 100);
   }
-  __device__ __forceinline__ int64_t of(int64_t t) const {  // range holding tile t
-    const int64_t x = t / blk, rem = t - x * blk;
-    return x * per + (rem < nh * ta ? rem / ta : nh + (rem - nh * ta) / tb);
+  __device__ __forceinline__ int64_t start(int64_t i) const {
+    if (!even) return min(W, i * r);
+    const int64_t x = div_by(i, per, lg_per), j = i - x * per;
+    if (x >= nblk) return W;
+    const int64_t b = block_start(x), S = block_start(x + 1) - b, A = half_tiles(S);
+    return j < nh ? b + div_by(j * A, nh, lg_nh) : b + A + div_by((j - nh) * (S - A), per - nh, lg_rest);
+  }
+  __device__ __forceinline__ int64_t of(int64_t t) const {  // range holding tile t < W
+    if (!even) return div_nn(t, r);
+    const int64_t x = div_nn((t + 1) * nblk - 1, W);
+    const int64_t b = block_start(x), S = block_start(x + 1) - b, A = half_tiles(S), u = t - b;
+    const int64_t j = u < A ? div_nn((u + 1) * nh - 1, A)
+                            : nh + div_nn((u - A + 1) * (per - nh) - 1, S - A);
+    return x * per + j;
   }
 };
 
@@ -210,21 +248,26 @@ __device__ __forceinline__ int64_t range_of_worker(int w, int workers) {
 template <bool FP8>
 __device__ __forceinline__ Ranges make_ranges(int64_t W, int Tmax, int workers, int P) {
   const int64_t rmin = max(int64_t(1), int64_t(Tmax + P - 3) / (P - 2));
-  const int skew = FP8 ? PKV_STREAM_SKEW_FP8 : 100;
-  const int nblk = range_blocks(workers);
-  Ranges r;
-  r.per = workers / nblk;
-  r.nh = r.per / 2;
-  if (skew == 100) {
-    r.ta = r.tb = max((W + workers - 1) / workers, rmin);
-  } else {
-    // W * skew / (skew + 100) tiles for the first half
-    const int64_t na = int64_t(nblk) * r.nh, nb = int64_t(nblk) * (r.per - r.nh);
-    r.ta = max((W * skew / (skew + 100) + na - 1) / na, rmin);
-    r.tb = max((max(W - na * r.ta, int64_t(0)) + nb - 1) / nb, rmin);
-  }
-  r.blk = r.nh * r.ta + (r.per - r.nh) * r.tb;
-  return r;
+  Ranges rg;
+  rg.W = max(W, int64_t(1));
+  rg.nblk = range_blocks(workers);
+  rg.per = workers / rg.nblk;
+  rg.nh = max(int64_t(1), rg.per / 2);
+  rg.skew = FP8 ? PKV_STREAM_SKEW_FP8 : 100;
+  if (rg.per < 2) rg.skew = 100;
+  rg.lg_nblk = log2_if_pow2(rg.nblk);
+  rg.lg_per = log2_if_pow2(rg.per);
+  rg.lg_nh = log2_if_pow2(rg.nh);
+  rg.lg_rest = log2_if_pow2(rg.per - rg.nh);
+  // shortest range of the even split: a block has at least floor(W / nblk)
+  // tiles, each half at least that times its share, less one for rounding
+  const int64_t smin = div_by(W, rg.nblk, rg.lg_nblk);
+  const int64_t amin = rg.skew == 100 ? smin >> 1 : div_nn(smin * 100, rg.skew + 100);
+  const int64_t shortest = min(div_by(amin, rg.nh, rg.lg_nh),
+                               div_nn(max(int64_t(0), smin - amin - 1), max(int64_t(1), rg.per - rg.nh))) - 1;
+  rg.even = rg.per >= 2 && shortest >= rmin;
+  rg.r = max(div_by(W + workers - 1, workers, log2_if_pow2(workers)), rmin);
+  return rg;
 }
 
 // What the loop needs to know about a tile besides its data.
@@ -365,9 +408,15 @@ struct StreamKernel {
     t.lo = live ? m.lo : 0;
   }
 
-  // Pieces the wave ranges cut segment m into.
-  static __device__ __forceinline__ int pieces_of(const Meta& m, const Ranges& rg) {
-    return int(rg.of(m.S + m.T - 1) - rg.of(m.S) + 1);
+  // The first and last range holding a tile of segment m, for a tile of m in
+  // range rw = [t0, t1), and the number of pieces the ranges cut it into.
+  static __device__ __forceinline__ int64_t first_range(const Meta& m, const Ranges& rg, int64_t rw,
+                                                        int64_t t0) {
+    return m.S >= t0 ? rw : rg.of(m.S);
+  }
+  static __device__ __forceinline__ int64_t last_range(const Meta& m, const Ranges& rg, int64_t rw,
+                                                       int64_t t1) {
+    return m.S + m.T <= t1 ? rw : rg.of(m.S + m.T - 1);
   }
 
   // Output rows of a segment that lies inside one wave's range: o / l.
@@ -430,12 +479,8 @@ struct StreamKernel {
     return prev;
   }
 
-  // The last piece to arrive combines the partials and re-arms the counter.
-  static __device__ __forceinline__ void finish(const DecodeArgs& a, int seg, int pieces, float* s_w) {
-    combine(a, seg, pieces, s_w);
-    if ((threadIdx.x & (kWave - 1)) == 0)
-      __hip_atomic_store(a.counters + seg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  // Vector memory loads that issue() enqueues for one tile.
+  static constexpr int kTileLoads = Geo::kKLoads + 4;
 
   // Float4 pieces of one partial (C rows of D) and how many each lane owns.
   static constexpr int kF4 = C * D / 4;
@@ -492,47 +537,60 @@ struct StreamKernel {
   }
 
   // Log-sum-exp combine of the `pieces` partials of segment seg's C columns
-  // (one wave; weights staged in LDS).  A lane owns float4 pieces of the C
-  // rows and keeps a batch of partials' loads in flight.
-  static __device__ __forceinline__ void combine(const DecodeArgs& a, int seg, int pieces,
-                                                 float* s_w) {
+  // (one wave; weights staged in LDS), done by the last piece to arrive,
+  // which then re-arms the counter.  A lane owns float4 pieces of the C rows.
+  // The loads of the statistics and of the first batch of partial rows all
+  // go out together (one round trip when pieces <= kBatch); a wave that
+  // finishes two segments issues both segments' loads before computing
+  // either.
+  static constexpr int kBatch = kOwn >= 16 ? 1 : 16 / kOwn;
+  static constexpr int kStat = (C * kMaxStepPartitions + kWave - 1) / kWave;
+  struct CombineLoads {
+    float mv[kStat], lv[kStat];
+    u32x4 v[kBatch][kOwn];
+  };
+
+  static __device__ __forceinline__ void load_batch(const DecodeArgs& a, __amdgpu_buffer_rsrc_t rs,
+                                                    int pieces, int p0, u32x4 (*v)[kOwn]) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+#pragma unroll
+      for (int k = 0; k < kOwn; ++k) {
+        const int c = lane + k * kWave;
+        v[q][k] = p0 + q < pieces && c < kF4 ? load16_coherent(rs, partial_offset(a, c, p0 + q))
+                                             : u32x4{0u, 0u, 0u, 0u};
+      }
+  }
+
+  static __device__ __forceinline__ void combine_issue(const DecodeArgs& a, int seg, int pieces,
+                                                       CombineLoads& ld) {
     const int lane = threadIdx.x & (kWave - 1);
     const size_t row0 = size_t(seg) * C;  // the segment's partial rows
-    constexpr int kBatch = kOwn >= 16 ? 1 : 16 / kOwn;
-    const __amdgpu_buffer_rsrc_t rs = partial_rows(a, row0);
-    // all loads of the statistics and of the first batch of partial rows go
-    // out together: one round trip when pieces <= kBatch
-    constexpr int kStat = (C * kMaxStepPartitions + kWave - 1) / kWave;
-    float mv[kStat], lv[kStat];
 #pragma unroll
     for (int i = 0; i < kStat; ++i) {
       const int t = lane + i * kWave;
-      mv[i] = lv[i] = 0.0f;
+      ld.mv[i] = ld.lv[i] = 0.0f;
       if (t < C * pieces) {
         const size_t pr = (row0 + t / pieces) * a.max_partitions + t % pieces;
-        mv[i] = load_f32_coherent(a.part_max + pr);
-        lv[i] = load_f32_coherent(a.part_sum + pr);
+        ld.mv[i] = load_f32_coherent(a.part_max + pr);
+        ld.lv[i] = load_f32_coherent(a.part_sum + pr);
       }
     }
-    u32x4 v[kBatch][kOwn];
-    auto load_batch = [&](int p0) {
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q)
-#pragma unroll
-        for (int k = 0; k < kOwn; ++k) {
-          const int c = lane + k * kWave;
-          v[q][k] = p0 + q < pieces && c < kF4 ? load16_coherent(rs, partial_offset(a, c, p0 + q))
-                                               : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    load_batch(0);
+    load_batch(a, partial_rows(a, row0), pieces, 0, ld.v);
+  }
+
+  static __device__ __forceinline__ void combine_finish(const DecodeArgs& a, int seg, int pieces,
+                                                        CombineLoads& ld, float* s_w) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const __amdgpu_buffer_rsrc_t rs = partial_rows(a, size_t(seg) * C);
 #pragma unroll
     for (int i = 0; i < kStat; ++i) {
       const int t = lane + i * kWave;
       if (t < C * pieces) {
         const int j = t / pieces, p = t % pieces;
-        s_w[2 * (j * kMaxStepPartitions + p)] = mv[i];
-        s_w[2 * (j * kMaxStepPartitions + p) + 1] = lv[i];
+        s_w[2 * (j * kMaxStepPartitions + p)] = ld.mv[i];
+        s_w[2 * (j * kMaxStepPartitions + p) + 1] = ld.lv[i];
       }
     }
     for (int j = lane; j < C; j += kWave) {
@@ -551,7 +609,7 @@ struct StreamKernel {
 #pragma unroll
     for (int k = 0; k < kOwn; ++k) num[k] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     for (int p0 = 0; p0 < pieces; p0 += kBatch) {
-      if (p0 > 0) load_batch(p0);
+      if (p0 > 0) load_batch(a, rs, pieces, p0, ld.v);
 #pragma unroll
       for (int q = 0; q < kBatch; ++q)
 #pragma unroll
@@ -559,7 +617,7 @@ struct StreamKernel {
           const int c = lane + k * kWave;
           if (p0 + q < pieces && c < kF4) {
             const float wgt = s_w[2 * ((4 * c / D) * kMaxStepPartitions + p0 + q) + 1];
-            num[k] += wgt * __builtin_bit_cast(float4_t, v[q][k]);
+            num[k] += wgt * __builtin_bit_cast(float4_t, ld.v[q][k]);
           }
         }
     }
@@ -576,6 +634,23 @@ struct StreamKernel {
                                     qrow(a, seg / a.Hkv, seg % a.Hkv, h) * D + 4 * c % D) = o;
       }
     }
+    if (lane == 0) __hip_atomic_store(a.counters + seg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  static __device__ __forceinline__ void finish(const DecodeArgs& a, int seg, int pieces, float* s_w) {
+    CombineLoads ld;
+    combine_issue(a, seg, pieces, ld);
+    combine_finish(a, seg, pieces, ld, s_w);
+  }
+
+  // Two segments finished by the same wave: one round trip for both.
+  static __device__ __forceinline__ void finish2(const DecodeArgs& a, int seg0, int pieces0, int seg1,
+                                                 int pieces1, float* s_w0, float* s_w1) {
+    CombineLoads l0, l1;
+    combine_issue(a, seg0, pieces0, l0);
+    combine_issue(a, seg1, pieces1, l1);
+    combine_finish(a, seg0, pieces0, l0, s_w0);
+    combine_finish(a, seg1, pieces1, l1, s_w1);
   }
 };
 
@@ -595,6 +670,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   const int jcol = n16 < C ? n16 / K::GRP(a) : 0;  // new query token of this lane's column
 
   __shared__ float s_w[2 * C * kMaxStepPartitions];  // combine weights
+  __shared__ float s_w2[2 * C * kMaxStepPartitions];  // a second segment's
   __shared__ float s_fin[K::kStage];                  // the range's last piece
   __shared__ float s_pend[K::kStage];                 // a piece that ended earlier
   // rotation angles of the positions of up to kDepth segments (QK-norm
@@ -619,7 +695,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   const int64_t t1 = min(W, rg.start(rw + 1));
 
   if (t0 < t1) {
-    Cursor cur = locate(a, B, t0, tot.per_head, L0, win);
+    Cursor cur = locate(a, B, t0, tot.per_head, L0, tot.incl0, win);
     int rope_b[K::kDepth];  // sequence whose angles are in each table
 #pragma unroll
     for (int i = 0; i < K::kDepth; ++i) rope_b[i] = -1;
@@ -691,12 +767,18 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
     }
 
     // A shared segment whose piece ends before the range does (only the
-    // range's first segment can) keeps its partial in LDS until the range is
-    // done.  Stores issued inside the loop would hold up the waits for the
-    // tiles behind them (vector memory operations complete in order), and
-    // the segment's last pieces end with the ranges anyway.
-    bool pend = false;
+    // range's first segment can: it is that segment's last piece) publishes
+    // its partial right away and arrives one loop step later, so that the
+    // segment's combine falls to one of the waves whose ranges end with its
+    // other pieces, and no wave has two combines to do when its range ends.
+    // The partial's stores go out behind the next tile's loads; one step
+    // later a counted wait that leaves the newest tile's loads in flight
+    // (vector memory operations complete in issue order) makes sure they
+    // have completed before the arrival, whose result is read when the
+    // range is done.
+    int pend = 0;  // 0 none, 1 partial written, 2 arrived (prev count in pprev)
     int pseg = 0, ppieces = 0, pj = 0;
+    uint32_t pprev = 0;
 
     // compute tile t (X, meta mx, q buffer qx); load tile t+NB-1 into Y
     // (meta my, q buffer qy)
@@ -730,7 +812,9 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
         return;
       }
       if (mx.last) {
-        const int pieces = K::pieces_of(mx, rg);
+        // the segment ends inside the range: its last range is this one
+        const int64_t r_first = K::first_range(mx, rg, rw, t0);
+        const int pieces = int(rw - r_first + 1);
         const int seg = mx.b * a.Hkv + mx.kvh;
         const float l = group4_sum(st.l);
         if (pieces == 1) {
@@ -739,12 +823,24 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
         } else {
           K::stage_partial(st, l, g, n16, s_pend);
           if constexpr (K::QKNORM) K::stash_q(s_q, qop, g, n16);
-          pend = true;
           pseg = seg;
           ppieces = pieces;
-          pj = int(rw - rg.of(mx.S));
+          pj = int(rw - r_first);
+          K::write_partial(a, size_t(pseg) * C, pj, s_pend);
+          pend = 1;
+          K::reset(st);
+          return;
         }
         K::reset(st);
+      }
+      if (pend == 1) {
+        // the partial's stores were issued before this step's tile loads;
+        // everything but the newest NB - 1 tiles' loads has completed
+        issue_fence();
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most((NB - 1) * K::kTileLoads));
+        issue_fence();
+        pprev = K::arrive(a, pseg);
+        pend = 2;
       }
     };
 
@@ -759,7 +855,8 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
 
     // the range's last piece
     const Meta& mf = mfin;
-    const int fpieces = K::pieces_of(mf, rg);
+    const int64_t f_first = K::first_range(mf, rg, rw, t0);
+    const int fpieces = int(K::last_range(mf, rg, rw, t1) - f_first + 1);
     const int fseg = mf.b * a.Hkv + mf.kvh;
     const float l = group4_sum(st.l);
     if (fpieces == 1) {
@@ -767,21 +864,31 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       if constexpr (K::QKNORM) K::write_q(a, fseg, qop, g, n16);
     } else {
       K::stage_partial(st, l, g, n16, s_fin);
-      K::write_partial(a, size_t(fseg) * C, int(rw - rg.of(mf.S)), s_fin);
+      K::write_partial(a, size_t(fseg) * C, int(rw - f_first), s_fin);
     }
-    if (pend) K::write_partial(a, size_t(pseg) * C, pj, s_pend);
-    if (pend || fpieces > 1) {
+    uint32_t fprev = 0;
+    if (pend == 1 || fpieces > 1) {
       __builtin_amdgcn_s_waitcnt(0);  // partials at device scope
-      const uint32_t pprev = pend ? K::arrive(a, pseg) : 0u;
-      const uint32_t fprev = fpieces > 1 ? K::arrive(a, fseg) : 0u;
-      if (pend && __builtin_amdgcn_readfirstlane(pprev) == uint32_t(ppieces - 1)) {
-        K::finish(a, pseg, ppieces, s_w);
-        if constexpr (K::QKNORM) K::write_q_stashed(a, pseg, s_q, g, n16);
+      if (pend == 1) {
+        pprev = K::arrive(a, pseg);
+        pend = 2;
       }
-      if (fpieces > 1 && __builtin_amdgcn_readfirstlane(fprev) == uint32_t(fpieces - 1)) {
-        K::finish(a, fseg, fpieces, s_w);
-        if constexpr (K::QKNORM) K::write_q(a, fseg, qop, g, n16);
-      }
+      if (fpieces > 1) fprev = K::arrive(a, fseg);
+    }
+    // the last arrival of a segment combines it; the early piece is rarely
+    // the last (its segment's other pieces end with their ranges)
+    const bool pfin = pend == 2 && __builtin_amdgcn_readfirstlane(pprev) == uint32_t(ppieces - 1);
+    const bool ffin = fpieces > 1 && __builtin_amdgcn_readfirstlane(fprev) == uint32_t(fpieces - 1);
+    if (pfin && ffin) {
+      K::finish2(a, pseg, ppieces, fseg, fpieces, s_w, s_w2);
+    } else if (pfin) {
+      K::finish(a, pseg, ppieces, s_w);
+    } else if (ffin) {
+      K::finish(a, fseg, fpieces, s_w);
+    }
+    if constexpr (K::QKNORM) {
+      if (pfin) K::write_q_stashed(a, pseg, s_q, g, n16);
+      if (ffin) K::write_q(a, fseg, qop, g, n16);
     }
   }
 
