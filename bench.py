@@ -43,17 +43,18 @@ ROTATE_BYTES = 1 << 30
 # workload and a hash of the step kernel's sources: a changed kernel reports
 # traffic null until it is measured again.
 STEP_SOURCES = ("decode_stream.hip", "decode_stream_cached.hip", "decode_stream_impl.h",
-                "decode_tile.h", "device.h", "kernels.h", "shape_limits.h")
-# The key's last field is the shared-blocks hint the run passed (bench.py
-# passes it for workloads whose tables share a prefix).
+                "decode_stream_prefix.hip", "decode_prefix_impl.h", "decode_tile.h", "device.h",
+                "kernels.h", "shape_limits.h")
+# The key's last two fields are the shared-blocks hint and the shared prefix
+# (in blocks) that the run passed.
 MEASURED_TRAFFIC = {
-    ("c2", "32f3f6bf4166b822", False): {"fetch_bytes": 316791232, "write_bytes": 3328384,
+    ("c2", "32f3f6bf4166b822", False, 0): {"fetch_bytes": 316791232, "write_bytes": 3328384,
                                         "source": "profiles/step_balanced_c2_hbm_bytes.md"},
-    ("c3", "32f3f6bf4166b822", True): {"fetch_bytes": 579730144, "write_bytes": 6058629,
+    ("c3", "32f3f6bf4166b822", True, 0): {"fetch_bytes": 579730144, "write_bytes": 6058629,
                                        "source": "profiles/step_balanced_c3_c4_c5_hbm_bytes.md"},
-    ("c4", "32f3f6bf4166b822", False): {"fetch_bytes": 4285991456, "write_bytes": 10026891,
+    ("c4", "32f3f6bf4166b822", False, 0): {"fetch_bytes": 4285991456, "write_bytes": 10026891,
                                         "source": "profiles/step_balanced_c3_c4_c5_hbm_bytes.md"},
-    ("c5", "32f3f6bf4166b822", False): {"fetch_bytes": 564210315, "write_bytes": 12873760,
+    ("c5", "32f3f6bf4166b822", False, 0): {"fetch_bytes": 564210315, "write_bytes": 12873760,
                                         "source": "profiles/step_balanced_c3_c4_c5_hbm_bytes.md"},
 }
 
@@ -99,6 +100,9 @@ def parse():
     p.add_argument("--paging-overhead", action="store_true",
                    help="also time the same steps with every sequence's blocks made "
                         "physically consecutive, and report the cost of paging itself")
+    p.add_argument("--prefix", default="auto", choices=("auto", "no"),
+                   help="auto: pass a shared prompt prefix (the prefix-shared config's 1024\n"
+                        "tokens) to the step as prefix_blocks, read once per group of sequences")
     p.add_argument("--shared-blocks", default="auto", choices=("auto", "yes", "no"),
                    help="pass the shared-blocks cache hint (auto: when the workload's tables "
                         "share a prefix)")
@@ -340,12 +344,26 @@ def main():
         return
 
     nq = args.n_query
+    # a chunk wider than one 16-column product (g * nq > 16) is appended by
+    # paged_kv_append (one slot per new token, QK-norm + RoPE at each token's
+    # position for the fused config) and then attended by the step
+    chunk = nq > 1 and cfg.group * nq > 16
     if nq > 1:
         # several new tokens per sequence: q and the new rows get a token axis
         rng = np.random.default_rng(208_300)
         d = dict(d, q=rng.standard_normal((cfg.B, nq, cfg.Hq, cfg.D)).astype(np.float16),
                  k_new=rng.standard_normal((cfg.B, nq, cfg.Hkv, cfg.D)).astype(np.float16),
                  v_new=rng.standard_normal((cfg.B, nq, cfg.Hkv, cfg.D)).astype(np.float16))
+        if chunk:
+            lens = d["context_lens"].astype(np.int64)
+            if int(lens.min()) < nq:
+                sys.exit(f"--n-query {nq} needs every context to hold the chunk (min L {lens.min()})")
+            tok = np.array([[L - nq + j + 1 for j in range(nq)] for L in lens], dtype=np.int32)
+            tab, BS = d["block_tables"], cfg.block_size
+            d["chunk_slots"] = np.array([[int(tab[b, (p - 1) // BS]) * BS + (p - 1) % BS
+                                          for p in tok[b]] for b in range(cfg.B)],
+                                        dtype=np.int64).reshape(-1)
+            d["chunk_lens"] = tok.reshape(-1)
         args.no_cpu_baseline = True
 
     cpu = None
@@ -387,6 +405,13 @@ def main():
     # the caller's block manager knows when tables share blocks (reference
     # counts); the hint only picks the KV loads' cache policy
     shared = (cfg.prefix_tokens > 0) if args.shared_blocks == "auto" else args.shared_blocks == "yes"
+    # the caller's block manager knows the shared prefix; the step then reads
+    # each prefix tile once per group of sequences
+    prefix_blocks = (cfg.prefix_tokens // cfg.block_size
+                     if args.prefix == "auto" and cfg.prefix_tokens and not args.unfused and nq == 1
+                     and not args.window and args.partition_size is None else 0)
+    if prefix_blocks and args.shared_blocks == "auto":
+        shared = False  # the prefix step picks the cache policy per tile itself
 
     def step_unfused(g, i, timed):
         if not fp8:
@@ -427,11 +452,24 @@ def main():
                           rope_theta=cfg.theta)
         if timed:
             ev["d0"][i].record(stream)
+        if chunk:
+            # the chunk's rows go in first (one launch), then the step attends
+            B_, Hkv_ = g["k_new"].shape[0], g["k_new"].shape[2]
+            akw = {}
+            if cfg.fused_append:
+                akw = dict(q=g["q"].view(B_ * nq, cfg.Hq, cfg.D), gamma_q=g["gamma_q"],
+                           gamma_k=g["gamma_k"], context_lens=g["chunk_lens"], eps=cfg.eps,
+                           rope_theta=cfg.theta)
+            if not fp8:
+                _lib.paged_kv_append(g["k_new"].view(B_ * nq, Hkv_, cfg.D),
+                                     g["v_new"].view(B_ * nq, Hkv_, cfg.D), g["k_pool"],
+                                     g["v_pool"], g["chunk_slots"], stream=stream, **akw)
+            kw = {}
         _lib.paged_decode_step(out, g["q"], g["k_pool"], g["v_pool"], g["block_tables"],
                                g["context_lens"], cfg.scale, k_scale=g.get("k_scale"),
                                v_scale=g.get("v_scale"), partition_size=step_ps,
-                               window=args.window, workspace=step_ws, shared_blocks=shared,
-                               stream=stream, **kw)
+                               window=args.window, prefix_blocks=prefix_blocks,
+                               workspace=step_ws, shared_blocks=shared, stream=stream, **kw)
         if timed:
             ev["d1"][i].record(stream)
 
@@ -538,8 +576,8 @@ def main():
     traffic = None
     fused_balanced = (not args.unfused and step_ps == 0 and args.splits == 16 and not args.window
                       and nq == 1)
-    measured = (MEASURED_TRAFFIC.get((cfg.name, step_source_hash(), shared)) if fused_balanced
-                else None)
+    measured = (MEASURED_TRAFFIC.get((cfg.name, step_source_hash(), shared, prefix_blocks))
+                if fused_balanced else None)
     if measured:
         traffic = measured["fetch_bytes"] + measured["write_bytes"]
     value = kv / (ms * 1e-3) / 1e9
@@ -576,11 +614,14 @@ def main():
             "step": ("attend+combine" if fp8 else
                      ("qknorm_rope+append+attend+combine" if cfg.fused_append
                       else "append+attend+combine")),
-            "launches_per_step": (3 if not fp8 else 2) if args.unfused and PS else 1,
+            "launches_per_step": ((3 if not fp8 else 2) if args.unfused and PS
+                                  else 2 if chunk and not fp8 else 1),
             "window": args.window,
             "new_tokens_per_sequence": nq,
+            "shared_prefix_blocks": prefix_blocks,
             "rotated_copies": R,
-            "kv_load_policy": "cached (shared-blocks hint)" if shared else "non-temporal",
+            "kv_load_policy": ("prefix tiles cached, own tiles non-temporal" if prefix_blocks
+                               else "cached (shared-blocks hint)" if shared else "non-temporal"),
         },
         "steps_per_s": round(1e3 / ms, 1),
         "tokens_per_s": round(cfg.B * nq * 1e3 / ms, 1),

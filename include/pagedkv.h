@@ -184,10 +184,10 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
  *   paged_attn_decode, at most 64 per sequence
  *   (ceil(MBS * BS / partition_size) <= 64), else PKV_EUNSUPPORTED.
  * part_out / part_max / part_sum: [B][Hq][max_partitions]([D]) fp32 scratch
- *   (contents undefined afterwards).  counters: [B][Hkv] uint32 device
- *   memory, all zero before the first call; each call leaves them zero
- *   again.  Calls sharing counters, scratch or pools must not run
- *   concurrently.
+ *   (contents undefined afterwards).  counters: [B][Hkv * CG] uint32 device
+ *   memory (CG = 1 unless n_query > 1 needs column groups, see below), all
+ *   zero before the first call; each call leaves them zero again.  Calls
+ *   sharing counters, scratch or pools must not run concurrently.
  * window > 0: sliding window ("Roadmap: vLLM-style serving features for
  *   TornadoVM batched decode", Models: Gemma 4's sliding-window layers):
  *   the query attends to positions max(0, L_b - window) .. L_b - 1 only, and
@@ -200,11 +200,37 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
  *   prefill puts several tokens of a sequence in one step).  q and out are
  *   [B][n_query][Hq][D], k_new / v_new [B][n_query][Hkv][D]; L_b counts the
  *   new tokens, which take positions L_b - n_query .. L_b - 1, and new token
- *   j attends to positions 0 .. L_b - n_query + j (causal).  The tokens share
- *   every KV byte read: they fill more columns of the same 16-wide products,
- *   so (Hq / Hkv) * n_query must be a power of two <= 16.  Balanced split
- *   only, no QK-norm, no window (else PKV_EUNSUPPORTED); part_* then hold
- *   [B][n_query * Hq][max_partitions]([D]).  L_b must be 0 or >= n_query.
+ *   j attends to positions 0 .. L_b - n_query + j (causal).  The query
+ *   columns of a (sequence, kv head), g = Hq / Hkv heads times n_query
+ *   tokens, fill the columns of 16-wide products that share every KV byte
+ *   read: up to 16 columns (a power of two) use one product, and the new
+ *   rows k_new / v_new may be appended in the same launch; more columns
+ *   (a multiple of 16, n_query <= 4096, e.g. a 512-token prefill chunk) are
+ *   split into CG = g * n_query / 16 column groups, each of which reads the
+ *   sequence's KV once, and the new rows must already be in the pools
+ *   (k_new == NULL: paged_kv_append with one slot per new token, with its
+ *   QK-norm + RoPE per token position if the model has them).  With
+ *   gamma_k != NULL (up to 8 columns, e.g. g = 4 and 2 tokens) each new
+ *   token's q and k are normalised and rotated at its own position.
+ *   Balanced split only, no window (else PKV_EUNSUPPORTED); part_* then
+ *   hold [B][n_query * Hq][max_partitions]([D]).  L_b must be 0 or >=
+ *   n_query.
+ * prefix_blocks > 0: the first prefix_blocks entries of every table row are
+ *   the same physical blocks, a shared prompt prefix ("Roadmap: vLLM-style
+ *   serving features for TornadoVM batched decode", Serving / scheduling:
+ *   a common prefix prefilled once into blocks all sequences map;
+ *   "Distributed LLM Inference Serving Platform", sections 2 and 11:
+ *   reference-counted shared blocks).  Each prefix tile is then read once
+ *   per group of 16 / (Hq / Hkv) sequences, whose q heads fill the columns
+ *   of the same products, instead of once per sequence.  Device-data
+ *   contract (not checked): those entries agree across the batch, and every
+ *   sequence has L_b == 0 or L_b > prefix_blocks * BS (the prefix holds
+ *   past tokens only, so the new row never lands in a shared block); a
+ *   sequence with 0 < L_b <= prefix_blocks * BS gets no output.  Balanced
+ *   split, n_query == 1, no window, no QK-norm (else PKV_EUNSUPPORTED),
+ *   max_partitions >= 6 (a sequence's prefix and own parts take up to
+ *   max_partitions / 2 pieces each); prefix_blocks < 0 or > MBS is
+ *   PKV_EINVAL.  0 = no shared prefix.
  * kv_dtype PKV_KV_E4M3: attend + combine only (k_new must be NULL); either
  *   dtype may carry PKV_KV_SHARED_BLOCKS.
  * L_b == 0: zero output row, nothing written to the pools, q untouched.
@@ -214,7 +240,8 @@ int paged_decode_step(void* out, void* q, const void* k_new, const void* v_new, 
                       void* v_pool, const float* k_scale, const float* v_scale,
                       const int32_t* block_tables, const int32_t* context_lens, int B, int Hq,
                       int Hkv, int D, int BS, int MBS, int64_t NB, float scale, int kv_dtype,
-                      int partition_size, int window, int n_query, const float* gamma_q,
+                      int partition_size, int window, int n_query, int prefix_blocks,
+                      const float* gamma_q,
                       const float* gamma_k, float eps, float rope_theta, float* part_out,
                       float* part_max, float* part_sum, uint32_t* counters, int max_partitions,
                       void* stream);
@@ -302,7 +329,7 @@ int paged_decode_step_static(void* out, void* q, const void* k_new, const void* 
                              const float* v_scale, const int32_t* block_tables,
                              const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
                              int MBS, int64_t NB, float scale, int kv_dtype, int partition_size,
-                             int window, int n_query, const float* gamma_q,
+                             int window, int n_query, int prefix_blocks, const float* gamma_q,
                              const float* gamma_k, float eps, float rope_theta, void* stream);
 
 /* Pieces per sequence paged_decode_step_static uses for these sizes (>= 1),
@@ -336,7 +363,8 @@ int pkv_validate_step(const void* out, const void* q, const void* k_new, const v
                       const float* v_scale, const int32_t* block_tables,
                       const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
                       int MBS, int64_t NB, float scale, int kv_dtype, int partition_size,
-                      int window, int n_query, const float* gamma_q, const float* gamma_k,
+                      int window, int n_query, int prefix_blocks, const float* gamma_q,
+                      const float* gamma_k,
                       float eps,
                       float rope_theta, const float* part_out, const float* part_max,
                       const float* part_sum, const uint32_t* counters, int max_partitions);

@@ -37,9 +37,10 @@ _SIGNATURES = {
                                _F, _I, _I, _P, _P, _P, _I, _P]),
     "paged_attn_reduce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "paged_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
-                               _I64, _F, _I, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I, _P]),
+                               _I64, _F, _I, _I, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I,
+                               _P]),
     "paged_decode_step_static": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
-                                      _I, _I64, _F, _I, _I, _I, _I, _P, _P, _F, _F, _P]),
+                                      _I, _I64, _F, _I, _I, _I, _I, _I, _P, _P, _F, _F, _P]),
     "paged_decode_step_static_partitions": (_I, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "paged_kv_copy_blocks": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I, _P]),
     "paged_kv_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P]),
@@ -54,7 +55,7 @@ _SIGNATURES = {
     "pkv_validate_copy": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I]),
     "pkv_validate_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64]),
     "pkv_validate_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
-                               _I64, _F, _I, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I]),
+                               _I64, _F, _I, _I, _I, _I, _I, _P, _P, _F, _F, _P, _P, _P, _P, _I]),
 }
 
 
@@ -308,24 +309,36 @@ def decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale, *, k_
     paged_attn_reduce(out, po, pm, ps, context_lens, partition_size, stream=stream)
 
 
+def step_column_groups(Hq_total, Hkv):
+    """16-column groups the query columns of one (sequence, kv head) are split
+    into: Hq_total = Hq * n_query columns per sequence, g * n_query per kv head."""
+    cols = Hq_total // Hkv
+    return cols // 16 if cols > 16 else 1
+
+
 def alloc_step_workspace(B, Hq, Hkv, D, max_partitions, device="cuda"):
-    """(part_out, part_max, part_sum, counters) for paged_decode_step; the
-    counters start at zero and every call leaves them at zero."""
+    """(part_out, part_max, part_sum, counters) for paged_decode_step, where Hq
+    counts every query row of a sequence (q heads times new tokens); the
+    counters (one per sequence, kv head and column group) start at zero and
+    every call leaves them at zero."""
     po, pm, ps = alloc_partials(B, Hq, D, max_partitions, device)
-    counters = torch.zeros((B, Hkv), dtype=torch.int32, device=device)
+    counters = torch.zeros((B, Hkv * step_column_groups(Hq, Hkv)), dtype=torch.int32,
+                           device=device)
     return po, pm, ps, counters
 
 
 def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale, *, k_new=None,
                       v_new=None, k_scale=None, v_scale=None, partition_size=0, window=0,
-                      gamma_q=None, gamma_k=None, eps=1e-6, rope_theta=1e6, workspace=None,
-                      shared_blocks=False, stream=None):
+                      prefix_blocks=0, gamma_q=None, gamma_k=None, eps=1e-6, rope_theta=1e6,
+                      workspace=None, shared_blocks=False, stream=None):
     """Append (optional, + Qwen3 QK-norm/RoPE) + decode + combine in one launch.
     ``workspace`` is alloc_step_workspace(...)'s tuple.  partition_size 0
     splits contexts evenly over all waves into at most workspace-depth
     pieces; > 0 uses fixed partitions.  window > 0 attends to the last
     `window` tokens only (balanced split).  shared_blocks: some blocks are
-    mapped by several tables (a shared prefix, forks): a cache-policy hint."""
+    mapped by several tables (a shared prefix, forks): a cache-policy hint.
+    prefix_blocks > 0: every table starts with these same blocks, which are
+    then read once per group of sequences."""
     nq = 1
     if q.dim() == 4:                      # [B, nq, Hq, D]: several new tokens per sequence
         nq = q.shape[1]
@@ -365,13 +378,14 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
     _check(ctr, "counters", torch.int32, 2)
     P = po.shape[2]
     if (tuple(po.shape) != (B, HqN, P, D) or tuple(pm.shape) != (B, HqN, P)
-            or tuple(ps.shape) != (B, HqN, P) or tuple(ctr.shape) != (B, Hkv)):
+            or tuple(ps.shape) != (B, HqN, P)
+            or tuple(ctr.shape) != (B, Hkv * step_column_groups(HqN, Hkv))):
         raise ValueError("workspace shapes disagree")
     st = lib().paged_decode_step(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
                                  _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                                  _ptr(context_lens), B, Hq, Hkv, D, BS, block_tables.shape[1], NB,
                                  float(scale), kv, int(partition_size), int(window), nq,
-                                 _ptr(gamma_q),
+                                 int(prefix_blocks), _ptr(gamma_q),
                                  _ptr(gamma_k), float(eps), float(rope_theta), _ptr(po), _ptr(pm),
                                  _ptr(ps), _ptr(ctr), P, _stream(stream))
     _raise("paged_decode_step", st)
@@ -388,8 +402,9 @@ def static_step_partitions(B, Hq, Hkv, D, BS, MBS, n_query=1, partition_size=0) 
 
 def paged_decode_step_static(out, q, k_pool, v_pool, block_tables, context_lens, scale, *,
                              k_new=None, v_new=None, k_scale=None, v_scale=None,
-                             partition_size=0, window=0, gamma_q=None, gamma_k=None, eps=1e-6,
-                             rope_theta=1e6, shared_blocks=False, stream=None):
+                             partition_size=0, window=0, prefix_blocks=0, gamma_q=None,
+                             gamma_k=None, eps=1e-6, rope_theta=1e6, shared_blocks=False,
+                             stream=None):
     """paged_decode_step with the library's static scratch instead of a
     workspace: allocates nothing.  Calls on one GPU must not overlap."""
     nq = 1
@@ -422,7 +437,8 @@ def paged_decode_step_static(out, q, k_pool, v_pool, block_tables, context_lens,
                                         _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
                                         _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, BS,
                                         block_tables.shape[1], NB, float(scale), kv,
-                                        int(partition_size), int(window), nq, _ptr(gamma_q),
+                                        int(partition_size), int(window), nq,
+                                        int(prefix_blocks), _ptr(gamma_q),
                                         _ptr(gamma_k), float(eps), float(rope_theta),
                                         _stream(stream))
     _raise("paged_decode_step_static", st)

@@ -113,6 +113,8 @@ extern "C" int paged_attn_decode(void* out, const void* q, const void* k_pool, c
   a.bs_tiles = 1;
   a.nq = 1;
   a.group = Hq / Hkv;
+  a.ncols = a.group;
+  a.cgroups = 1;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.MBS = MBS;
@@ -141,15 +143,15 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
                                  const int32_t* context_lens, int B, int Hq, int Hkv, int D,
                                  int BS, int MBS, int64_t NB, float scale, int kv_dtype,
                                  int partition_size, int window, int n_query,
-                                 const float* gamma_q, const float* gamma_k, float eps,
-                                 float rope_theta, float* part_out, float* part_max,
+                                 int prefix_blocks, const float* gamma_q, const float* gamma_k,
+                                 float eps, float rope_theta, float* part_out, float* part_max,
                                  float* part_sum, uint32_t* counters, int max_partitions,
                                  void* stream) {
   const int st = pkv_validate_step(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
                                    block_tables, context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale,
-                                   kv_dtype, partition_size, window, n_query, gamma_q, gamma_k,
-                                   eps, rope_theta, part_out, part_max, part_sum, counters,
-                                   max_partitions);
+                                   kv_dtype, partition_size, window, n_query, prefix_blocks,
+                                   gamma_q, gamma_k, eps, rope_theta, part_out, part_max,
+                                   part_sum, counters, max_partitions);
   if (st != PKV_OK || B == 0) return st;
   const bool fp8 = (kv_dtype & ~PKV_KV_SHARED_BLOCKS) == PKV_KV_E4M3;
   pkv::DecodeArgs a{};
@@ -170,6 +172,9 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
   a.bs_shift = a.bs_tiles == 2 ? 1 : 0;
   a.nq = n_query;
   a.group = Hq / Hkv;
+  a.ncols = a.group * n_query;
+  a.cgroups = a.ncols > pkv::kColsPerProduct ? a.ncols / pkv::kColsPerProduct : 1;
+  a.prefix_tiles = prefix_blocks * a.bs_tiles;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.MBS = MBS;
@@ -186,9 +191,12 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
   int mode = pkv::kModeCombine;
   if (k_new) mode |= pkv::kModeAppend;
   if (gamma_k) mode |= pkv::kModeQkNorm;
-  if (partition_size == 0)  // balanced split across a fixed number of waves
-    return launch_status(pkv::launch_decode_stream(a, B, D, (Hq / Hkv) * n_query, fp8, mode,
+  if (prefix_blocks > 0)  // balanced split, shared prefix read once per group of sequences
+    return launch_status(pkv::launch_decode_prefix(a, B, D, a.ncols, fp8, mode,
                                                    static_cast<hipStream_t>(stream)));
+  if (partition_size == 0)  // balanced split across a fixed number of waves
+    return launch_status(pkv::launch_decode_stream(a, B, D, a.cgroups > 1 ? pkv::kColsPerProduct : a.ncols,
+                                                   fp8, mode, static_cast<hipStream_t>(stream)));
   return launch_status(pkv::launch_decode_step(a, B, D, Hq / Hkv, fp8, mode,
                                                static_cast<hipStream_t>(stream)));
 }
@@ -237,7 +245,9 @@ extern "C" int paged_decode_step_static_partitions(int B, int Hq, int Hkv, int D
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || MBS <= 0 || n_query < 1 ||
       partition_size < 0)
     return PKV_EINVAL;
-  if (int64_t(B) * Hkv * int64_t(sizeof(uint32_t)) > int64_t(kScratchCounterBytes))
+  const int64_t cols = int64_t(Hq / Hkv) * n_query;
+  const int64_t cgroups = cols > pkv::kColsPerProduct ? (cols + pkv::kColsPerProduct - 1) / pkv::kColsPerProduct : 1;
+  if (int64_t(B) * Hkv * cgroups * int64_t(sizeof(uint32_t)) > int64_t(kScratchCounterBytes))
     return PKV_ENOSPACE;
   // bytes of one partial slot of every output row
   const int64_t per_slot = int64_t(B) * Hq * n_query * (int64_t(D) + 2) * int64_t(sizeof(float));
@@ -260,8 +270,9 @@ extern "C" int paged_decode_step_static(void* out, void* q, const void* k_new, c
                                         const int32_t* context_lens, int B, int Hq, int Hkv, int D,
                                         int BS, int MBS, int64_t NB, float scale, int kv_dtype,
                                         int partition_size, int window, int n_query,
-                                        const float* gamma_q, const float* gamma_k, float eps,
-                                        float rope_theta, void* stream) {
+                                        int prefix_blocks, const float* gamma_q,
+                                        const float* gamma_k, float eps, float rope_theta,
+                                        void* stream) {
   const int P = paged_decode_step_static_partitions(B, Hq, Hkv, D, BS, MBS, n_query,
                                                     partition_size);
   if (P < 0) return P;
@@ -276,13 +287,14 @@ extern "C" int paged_decode_step_static(void* out, void* q, const void* k_new, c
   float* part_sum = part_max + rows;
   const int st = pkv_validate_step(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale,
                                    block_tables, context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale,
-                                   kv_dtype, partition_size, window, n_query, gamma_q, gamma_k,
-                                   eps, rope_theta, part_out, part_max, part_sum, counters, P);
+                                   kv_dtype, partition_size, window, n_query, prefix_blocks,
+                                   gamma_q, gamma_k, eps, rope_theta, part_out, part_max, part_sum,
+                                   counters, P);
   if (st != PKV_OK || B == 0) return st;
   const int sf = scratch_fill_once(dev, base, static_cast<hipStream_t>(stream));
   if (sf != PKV_OK) return sf;
   return paged_decode_step(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_tables,
                            context_lens, B, Hq, Hkv, D, BS, MBS, NB, scale, kv_dtype,
-                           partition_size, window, n_query, gamma_q, gamma_k, eps, rope_theta,
-                           part_out, part_max, part_sum, counters, P, stream);
+                           partition_size, window, n_query, prefix_blocks, gamma_q, gamma_k, eps,
+                           rope_theta, part_out, part_max, part_sum, counters, P, stream);
 }

@@ -65,8 +65,13 @@ constexpr int stream_waves_per_eu() {
 }
 
 // Position of one tile in the flattened order.
+// A segment is one (sequence, kv head, column group): with cg > 1 column
+// groups the query columns of a sequence (g heads times its new tokens) are
+// split over cg 16-column products, each of which reads the sequence's
+// tiles once.
 struct Cursor {
   int b, kvh, n;  // sequence, kv head, tile within the segment
+  int cg;         // column group
   int L, T;       // context length of b, tiles per segment
   int f;          // block-table index of the segment's first tile
   int64_t S;      // flattened index of the segment's first tile
@@ -109,14 +114,14 @@ struct Totals {
 
 // L0: this lane's length in the first chunk of 64 sequences, read once by
 // the caller and used by both scans.
-__device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B, int L0, int W) {
+__device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B, int L0, int W, int CG) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t tot = 0;
   int mx = 0, incl0 = 0;
   for (int c = 0; c < B; c += kWave) {
     const int b = c + lane;
     const int T = seg_tiles(c == 0 ? L0 : b < B ? a.context_lens[b] : 0, W);
-    const int incl = wave_scan(T);
+    const int incl = wave_scan(T * CG);
     if (c == 0) incl0 = incl;
     tot += __builtin_amdgcn_readlane(incl, kWave - 1);
     mx = max(mx, T);
@@ -128,7 +133,7 @@ __device__ __forceinline__ Totals total_tiles(const DecodeArgs& a, int B, int L0
 
 // Cursor of flattened tile t (t < total); wh = tiles of one kv head.
 __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, int64_t wh, int L0,
-                                        int incl0, int W) {
+                                        int incl0, int W, int CG) {
   const int lane = threadIdx.x & (kWave - 1);
   Cursor c{};
   c.kvh = int(div_nn(t, wh));
@@ -137,7 +142,7 @@ __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, 
   for (int c0 = 0; c0 < B; c0 += kWave) {
     const int b = c0 + lane;
     const int L = c0 == 0 ? L0 : b < B ? a.context_lens[b] : 0;
-    const int w = seg_tiles(L, W);
+    const int w = seg_tiles(L, W) * CG;
     const int incl = c0 == 0 ? incl0 : wave_scan(w);
     const int64_t hi = carry + incl;
     const int64_t lo = hi - w;
@@ -149,8 +154,10 @@ __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, 
       c.T = seg_tiles(c.L, W);
       c.f = first_tile(c.L, W);
       const int64_t lo_src = carry + __builtin_amdgcn_readlane(incl - w, src);
-      c.n = int(r - lo_src);
-      c.S = int64_t(c.kvh) * wh + lo_src;
+      const int nn = int(r - lo_src);  // tile within the sequence's cg segments
+      c.cg = CG == 1 ? 0 : nn / c.T;
+      c.n = nn - c.cg * c.T;
+      c.S = int64_t(c.kvh) * wh + lo_src + int64_t(c.cg) * c.T;
       return c;
     }
     carry += __builtin_amdgcn_readlane(incl, kWave - 1);
@@ -160,10 +167,12 @@ __device__ __forceinline__ Cursor locate(const DecodeArgs& a, int B, int64_t t, 
 
 // Next tile in the flattened order (skips sequences with no tokens); past
 // the last tile c.b == B.
-__device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B, int W) {
+__device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B, int W, int CG) {
   if (++c.n < c.T) return;
   c.n = 0;
   c.S += c.T;
+  if (++c.cg < CG) return;  // the sequence's next column group
+  c.cg = 0;
   do {
     if (++c.b >= B) {
       c.b = 0;
@@ -273,6 +282,9 @@ __device__ __forceinline__ Ranges make_ranges(int64_t W, int Tmax, int workers, 
 // What the loop needs to know about a tile besides its data.
 struct Meta {
   int b, kvh, n, L, T, f;
+  int cg;      // column group
+  int kind;    // shared-prefix step: 1 a group's prefix span, 0 a sequence's own tiles
+  int grp;     // shared-prefix step: the group
   int lo;      // rows of the tile before the window (first tile only)
   int id;      // physical block of the tile
   int half;    // which 16-token tile of a 32-token block
@@ -294,6 +306,7 @@ __device__ __forceinline__ Meta meta_of(const Cursor& c, const DecodeArgs& a, in
   m.lo = c.n == 0 ? window_start(c.L, W) - 16 * c.f : 0;
   m.b = c.b;
   m.kvh = c.kvh;
+  m.cg = c.cg;
   m.n = c.n;
   m.L = c.L;
   m.T = c.T;
@@ -317,16 +330,36 @@ struct StreamKernel {
   static __device__ __forceinline__ int GRP(const DecodeArgs& a) { return EXT ? a.group : C; }
   static __device__ __forceinline__ int BST(const DecodeArgs& a) { return EXT ? a.bs_tiles : 1; }
   static __device__ __forceinline__ int BSS(const DecodeArgs& a) { return EXT ? a.bs_shift : 0; }
+  // column groups per (sequence, kv head) and query columns per (sequence,
+  // kv head): g * nq; with more than one group each holds C = 16 columns
+  static __device__ __forceinline__ int CG(const DecodeArgs& a) { return EXT ? a.cgroups : 1; }
+  static __device__ __forceinline__ int NCOLS(const DecodeArgs& a) { return EXT ? a.ncols : C; }
   static constexpr bool APPEND = (MODE & kModeAppend) != 0;
   static constexpr bool QKNORM = (MODE & kModeQkNorm) != 0;
   // tiles in the load pipeline of a wave
   static constexpr int kDepth = PKV_STREAM_DEPTH;
 
-  // The C columns of a segment's 16-wide products: column col is new query
-  // token col / g of q head kvh * g + col % g (g = Hq / Hkv; one new token
-  // per sequence unless nq > 1).  Row of q and of out [B][nq][Hq][D]:
+  // The columns of a segment's 16-wide products: query column col (0 ..
+  // g * nq - 1 of the sequence and kv head) is new query token col / g of q
+  // head kvh * g + col % g (g = Hq / Hkv; one new token per sequence unless
+  // nq > 1); column group cg holds columns cg * C .. cg * C + C - 1.  Row of
+  // q and of out [B][nq][Hq][D]:
   static __device__ __forceinline__ size_t qrow(const DecodeArgs& a, int b, int kvh, int col) {
     return (size_t(b) * NQ(a) + col / GRP(a)) * a.Hq + kvh * GRP(a) + col % GRP(a);
+  }
+  // A segment's index (its arrival counter) and, from it, its sequence, kv
+  // head and column group; its partial rows start at row0 (one row per query
+  // column, in (sequence, kv head, column) order).
+  static __device__ __forceinline__ int seg_id(const DecodeArgs& a, int b, int kvh, int cg) {
+    return (b * a.Hkv + kvh) * CG(a) + cg;
+  }
+  static __device__ __forceinline__ size_t seg_row0(const DecodeArgs& a, int seg) {
+    const int bk = CG(a) == 1 ? seg : seg / CG(a);
+    return size_t(bk) * NCOLS(a) + size_t(seg - bk * CG(a)) * C;
+  }
+  static __device__ __forceinline__ size_t seg_qrow(const DecodeArgs& a, int seg, int col) {
+    const int bk = CG(a) == 1 ? seg : seg / CG(a);
+    return qrow(a, bk / a.Hkv, bk % a.Hkv, (seg - bk * CG(a)) * C + col);
   }
 
   // q of head slot n16 of the segment's group, laid out as the B operand of
@@ -335,12 +368,12 @@ struct StreamKernel {
   // that a load is still filling.  QK-norm is applied when the segment's
   // first tile is computed, once the loads have landed.
   static __device__ __forceinline__ void load_q(half8_t* qop, const DecodeArgs& a, int b, int kvh,
-                                                int g, int n16) {
+                                                int cg, int g, int n16) {
     const size_t base = size_t(b) * NQ(a) * a.Hq;
     const _Float16* qs = static_cast<const _Float16*>(a.q) + base * D;
     const int span = NQ(a) * a.Hq * D;  // the sequence's q rows
     const __amdgpu_buffer_rsrc_t r = make_rsrc(qs, span * int(sizeof(_Float16)));
-    const int row = n16 < C ? int(qrow(a, b, kvh, n16) - base) * D : span;
+    const int row = n16 < C ? int(qrow(a, b, kvh, cg * C + n16) - base) * D : span;
 #pragma unroll
     for (int c = 0; c < Geo::kQK; ++c)
       qop[c] = __builtin_bit_cast(half8_t, buffer_load16(r, (row + qk_dim0<FP8>(c, g)) * int(sizeof(_Float16))));
@@ -388,9 +421,11 @@ struct StreamKernel {
             *reinterpret_cast<u32x4*>(kt + k_off + k * 64) = __builtin_bit_cast(u32x4, kc[k]);
         if (g == r_new / 4) *reinterpret_cast<VW*>(vt + v_off + (r_new % 4) * Geo::kRow) = vc;
       }
-      // on to the next segment
+      // on to the next segment (the new rows are written once, by the
+      // column group 0 segment; more groups exist only without an append)
       c.n = c.T - 1;
-      advance(c, a, B, W(a));
+      c.cg = CG(a) - 1;
+      advance(c, a, B, W(a), CG(a));
       if (c.b >= B) break;
     }
   }
@@ -424,7 +459,7 @@ struct StreamKernel {
                                                       const DecodeArgs& a, int seg, int g, int n16) {
     if (n16 >= C) return;
     const float inv = 1.0f / l;
-    _Float16* o = static_cast<_Float16*>(a.out) + qrow(a, seg / a.Hkv, seg % a.Hkv, n16) * D;
+    _Float16* o = static_cast<_Float16*>(a.out) + seg_qrow(a, seg, n16) * D;
     typedef _Float16 hv __attribute__((ext_vector_type(Geo::kPV)));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -448,8 +483,7 @@ struct StreamKernel {
   static __device__ __forceinline__ void write_q(const DecodeArgs& a, int seg, const half8_t* qop,
                                                  int g, int n16) {
     if (n16 >= C) return;
-    _Float16* qh = const_cast<_Float16*>(static_cast<const _Float16*>(a.q)) +
-                   qrow(a, seg / a.Hkv, seg % a.Hkv, n16) * D;
+    _Float16* qh = const_cast<_Float16*>(static_cast<const _Float16*>(a.q)) + seg_qrow(a, seg, n16) * D;
 #pragma unroll
     for (int c = 0; c < Geo::kQK; ++c)
       *reinterpret_cast<u32x4*>(qh + qk_dim0<false>(c, g)) = __builtin_bit_cast(u32x4, qop[c]);
@@ -566,7 +600,7 @@ struct StreamKernel {
   static __device__ __forceinline__ void combine_issue(const DecodeArgs& a, int seg, int pieces,
                                                        CombineLoads& ld) {
     const int lane = threadIdx.x & (kWave - 1);
-    const size_t row0 = size_t(seg) * C;  // the segment's partial rows
+    const size_t row0 = seg_row0(a, seg);  // the segment's partial rows
 #pragma unroll
     for (int i = 0; i < kStat; ++i) {
       const int t = lane + i * kWave;
@@ -583,7 +617,7 @@ struct StreamKernel {
   static __device__ __forceinline__ void combine_finish(const DecodeArgs& a, int seg, int pieces,
                                                         CombineLoads& ld, float* s_w) {
     const int lane = threadIdx.x & (kWave - 1);
-    const __amdgpu_buffer_rsrc_t rs = partial_rows(a, size_t(seg) * C);
+    const __amdgpu_buffer_rsrc_t rs = partial_rows(a, seg_row0(a, seg));
 #pragma unroll
     for (int i = 0; i < kStat; ++i) {
       const int t = lane + i * kWave;
@@ -630,8 +664,8 @@ struct StreamKernel {
         half4_t o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = (_Float16)(num[k][e] / den);
-        *reinterpret_cast<half4_t*>(static_cast<_Float16*>(a.out) +
-                                    qrow(a, seg / a.Hkv, seg % a.Hkv, h) * D + 4 * c % D) = o;
+        *reinterpret_cast<half4_t*>(static_cast<_Float16*>(a.out) + seg_qrow(a, seg, h) * D +
+                                    4 * c % D) = o;
       }
     }
     if (lane == 0) __hip_atomic_store(a.counters + seg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -667,7 +701,6 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   const int n16 = lane % 16;
   const int k_off = n16 * Geo::kRow + g * 16;
   const int v_off = (4 * g) * Geo::kRow + n16 * Geo::kVBytes;
-  const int jcol = n16 < C ? n16 / K::GRP(a) : 0;  // new query token of this lane's column
 
   __shared__ float s_w[2 * C * kMaxStepPartitions];  // combine weights
   __shared__ float s_w2[2 * C * kMaxStepPartitions];  // a second segment's
@@ -677,15 +710,16 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   // modes): a segment's table is written when its first tile is issued and
   // read when that tile is computed, and at most kDepth - 1 tiles are issued
   // in between, so kDepth tables taken in turn never overwrite one in use
-  __shared__ float s_cos[K::QKNORM ? K::kDepth * (D / 2) : 1];
-  __shared__ float s_sin[K::QKNORM ? K::kDepth * (D / 2) : 1];
+  // (one table per new token of the segment: nq <= C / g tokens)
+  __shared__ float s_cos[K::QKNORM ? K::kDepth * C * (D / 2) : 1];
+  __shared__ float s_sin[K::QKNORM ? K::kDepth * C * (D / 2) : 1];
   __shared__ _Float16 s_q[K::QKNORM ? C * D : 1];
   __shared__ double s_f[K::QKNORM ? D / 2 : 1];      // rotation frequencies
   __shared__ float s_gq[K::QKNORM ? D : 1];          // RMSNorm weights of q and k
   __shared__ float s_gk[K::QKNORM ? D : 1];
 
   const int L0 = lane < B ? a.context_lens[lane] : 0;
-  const Totals tot = total_tiles(a, B, L0, win);
+  const Totals tot = total_tiles(a, B, L0, win, K::CG(a));
   const int64_t W = tot.tiles;
   // equal shares, but long enough that no sequence's segment is cut into more
   // than max_partitions pieces: T tiles span at most (T-1)/tpw + 2 ranges
@@ -695,7 +729,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   const int64_t t1 = min(W, rg.start(rw + 1));
 
   if (t0 < t1) {
-    Cursor cur = locate(a, B, t0, tot.per_head, L0, tot.incl0, win);
+    Cursor cur = locate(a, B, t0, tot.per_head, L0, tot.incl0, win, K::CG(a));
     int rope_b[K::kDepth];  // sequence whose angles are in each table
 #pragma unroll
     for (int i = 0; i < K::kDepth; ++i) rope_b[i] = -1;
@@ -713,7 +747,10 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       m.slot = ord++ % K::kDepth;
       if constexpr (K::QKNORM) {
         if (m.b != rope_b[m.slot]) {
-          rope_angles<D>(s_f, s_cos + m.slot * (D / 2), s_sin + m.slot * (D / 2), m.L - 1);
+          // token j of the nq new ones sits at position L - nq + j
+          for (int j = 0; j < K::NQ(a); ++j)
+            rope_angles<D>(s_f, s_cos + (m.slot * C + j) * (D / 2), s_sin + (m.slot * C + j) * (D / 2),
+                           m.L - K::NQ(a) + j);
           rope_b[m.slot] = m.b;
         }
       }
@@ -740,7 +777,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
     auto take = [&](Meta& m, half8_t* qdst) {
       if (m.first) {
         prepare_segment(m);
-        K::load_q(qdst, a, m.b, m.kvh, g, n16);
+        K::load_q(qdst, a, m.b, m.kvh, m.cg, g, n16);
       } else {
         m.slot = last_slot;
       }
@@ -754,7 +791,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
     for (int k = 1; k < NB; ++k) {
       const bool live = t0 + k < t1;
       if (live) {
-        advance(cur, a, B, win);
+        advance(cur, a, B, win, K::CG(a));
         Meta m = meta_of(cur, a, t0 + k, t0, t1, win, K::BST(a), K::BSS(a));
         if (k < NB - 1) {
           mt[k] = m;
@@ -791,7 +828,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       }
       K::issue(y, a, my, live, k_off, v_off);
       if (t + NB < t1) {
-        advance(cur, a, B, win);
+        advance(cur, a, B, win, K::CG(a));
         ahead = meta_of(cur, a, t + NB, t0, t1, win, K::BST(a), K::BSS(a));
       }
       issue_fence();  // Y's loads stay ahead of the waits below
@@ -799,12 +836,17 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
 #pragma unroll
         for (int c = 0; c < Geo::kQK; ++c) qop[c] = qx[c];
         if constexpr (K::QKNORM)
-          norm_rope_chunks<D>(qop, s_gq, a.eps, s_cos + mx.slot * (D / 2),
-                              s_sin + mx.slot * (D / 2), g);
+        {
+          // the lane's column belongs to new token (column / g)
+          const int tq = min(n16, C - 1) / K::GRP(a);
+          norm_rope_chunks<D>(qop, s_gq, a.eps, s_cos + (mx.slot * C + tq) * (D / 2),
+                              s_sin + (mx.slot * C + tq) * (D / 2), g);
+        }
       }
       issue_fence();
       // causal limit of this lane's column: new token j sees positions up to
       // L - nq + j (rows of tile f + n at or past the limit are masked)
+      const int jcol = EXT ? (mx.cg * C + min(n16, C - 1)) / K::GRP(a) : 0;
       const int col_hi = EXT ? mx.L - K::NQ(a) + 1 + jcol - 16 * (mx.f + mx.n) : 16;
       mfma_tile<D, FP8>(st, x, qop, a.scale_log2, g, col_hi);
       if (t + 1 >= t1) {
@@ -815,7 +857,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
         // the segment ends inside the range: its last range is this one
         const int64_t r_first = K::first_range(mx, rg, rw, t0);
         const int pieces = int(rw - r_first + 1);
-        const int seg = mx.b * a.Hkv + mx.kvh;
+        const int seg = K::seg_id(a, mx.b, mx.kvh, mx.cg);
         const float l = group4_sum(st.l);
         if (pieces == 1) {
           K::store_direct(st, l, a, seg, g, n16);
@@ -826,7 +868,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
           pseg = seg;
           ppieces = pieces;
           pj = int(rw - r_first);
-          K::write_partial(a, size_t(pseg) * C, pj, s_pend);
+          K::write_partial(a, K::seg_row0(a, pseg), pj, s_pend);
           pend = 1;
           K::reset(st);
           return;
@@ -857,14 +899,14 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
     const Meta& mf = mfin;
     const int64_t f_first = K::first_range(mf, rg, rw, t0);
     const int fpieces = int(K::last_range(mf, rg, rw, t1) - f_first + 1);
-    const int fseg = mf.b * a.Hkv + mf.kvh;
+    const int fseg = K::seg_id(a, mf.b, mf.kvh, mf.cg);
     const float l = group4_sum(st.l);
     if (fpieces == 1) {
       K::store_direct(st, l, a, fseg, g, n16);
       if constexpr (K::QKNORM) K::write_q(a, fseg, qop, g, n16);
     } else {
       K::stage_partial(st, l, g, n16, s_fin);
-      K::write_partial(a, size_t(fseg) * C, int(rw - f_first), s_fin);
+      K::write_partial(a, K::seg_row0(a, fseg), int(rw - f_first), s_fin);
     }
     uint32_t fprev = 0;
     if (pend == 1 || fpieces > 1) {
@@ -938,7 +980,8 @@ hipError_t launch_stream_mode(const DecodeArgs& a, int B, int mode, hipStream_t 
       case kModeAppend | kModeCombine:
         return launch_stream<D, C, false, kModeAppend | kModeCombine, CACHED>(a, B, stream);
       case kModeAppend | kModeQkNorm | kModeCombine:
-        // QK-norm runs with one new token per sequence: at most 8 columns
+        // QK-norm runs with at most 8 query columns (g * nq): one rotation
+        // table per new token and pipeline slot in LDS
         if constexpr (C <= 8)
           return launch_stream<D, C, false, kModeAppend | kModeQkNorm | kModeCombine, CACHED>(
               a, B, stream);

@@ -303,19 +303,20 @@ __device__ __forceinline__ void mfma_tile(MState<D, FP8>& st, const MTile<D, FP8
 #pragma unroll
   for (int c = 0; c < Geo::kQK; ++c)
     s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<D, FP8>(t, c), qop[c], s, 0, 0, 0);
-  // logits in log2 units; rows outside [lo, min(rows, col_hi)) are masked
-  // after the scaling, so a zero E4M3 K scale (a block whose rows are all
-  // zero) gives zero logits, never -inf * 0
-  const float cs = scale_log2 * t.ks;
+  // logit factor in log2 units.  An E4M3 K scale of 0 (a block whose rows
+  // are all zero) is replaced by 1e-30: the masked rows' -inf must not meet a
+  // zero factor (-inf * 0 is NaN), and the valid rows' logits stay ~1e-27,
+  // whose exp2 rounds exactly as that of 0 in fp32.
+  const float cs = scale_log2 * (t.ks != 0.0f ? t.ks : 1e-30f);
   float tm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    s[r] = (4 * g + r) < min(t.rows, col_hi) && (4 * g + r) >= t.lo ? s[r] * cs : -INFINITY;
+    s[r] = (4 * g + r) < min(t.rows, col_hi) && (4 * g + r) >= t.lo ? s[r] : -INFINITY;
     tm = fmaxf(tm, s[r]);
   }
   // the head's 16 tokens sit in lanes n16, n16+16, n16+32, n16+48
   tm = group4_max(tm);
-  const float mn = fmaxf(st.m, tm);
+  const float mn = fmaxf(st.m, tm * cs);
   const float alpha = fast_exp2(st.m - mn);
   st.m = mn;
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // skip the rescale when no max moved
@@ -326,7 +327,7 @@ __device__ __forceinline__ void mfma_tile(MState<D, FP8>& st, const MTile<D, FP8
   float p[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    p[r] = fast_exp2(s[r] - mn);
+    p[r] = fast_exp2(fmaf(s[r], cs, -mn));
     st.l += p[r];
   }
   half4_t pv;

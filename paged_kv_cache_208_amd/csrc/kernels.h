@@ -31,6 +31,9 @@ struct DecodeArgs {
   uint32_t* counters;         // [B][Hkv] arrivals per (sequence, kv head); zero between launches
   int window;                 // > 0: attend to the last `window` tokens only (balanced step)
   int nq;                     // new query tokens per sequence (balanced step; 1 otherwise)
+  int ncols;                  // query columns per (sequence, kv head): group * nq
+  int cgroups;                // 16-column groups they are split into (1 when ncols <= 16)
+  int prefix_tiles;           // > 0: every table starts with these shared 16-token tiles
   int group;                  // Hq / Hkv
   int bs_tiles;               // 16-token tiles per block: 1, or 2 for 32-token blocks
   int bs_shift;               // log2(bs_tiles)
@@ -99,6 +102,9 @@ hipError_t launch_decode_step(const DecodeArgs& a, int B, int D, int group, bool
                               hipStream_t stream);
 // cols = (Hq / Hkv) * nq, the used columns of the 16-wide products (1..16)
 hipError_t launch_decode_stream(const DecodeArgs& a, int B, int D, int cols, bool fp8, int mode,
+                                hipStream_t stream);
+// tables that all start with a.prefix_tiles shared tiles (cols = Hq / Hkv)
+hipError_t launch_decode_prefix(const DecodeArgs& a, int B, int D, int cols, bool fp8, int mode,
                                 hipStream_t stream);
 // the same with the default cache policy for the KV tiles (shared-blocks hint)
 hipError_t launch_decode_stream_cached(const DecodeArgs& a, int B, int D, int cols, bool fp8,

@@ -12,4 +12,7 @@ constexpr int64_t kMaxGrid = (int64_t(1) << 24) - 1;  // workgroups per launch (
 constexpr int64_t kMaxAppendRows = int64_t(1) << 24;
 constexpr int kMaxStepPartitions = 64;     // partitions one step combines in-kernel
 constexpr int kStaticStepPartitions = 16;  // pieces per sequence of the static-scratch step
+constexpr int kColsPerProduct = 16;        // query columns of one 16-wide MFMA product
+constexpr int kMaxNewTokens = 4096;        // new query tokens per sequence in one step
+constexpr int kQkNormCols = 8;             // query columns of the QK-norm step (g * nq)
 }  // namespace pkv

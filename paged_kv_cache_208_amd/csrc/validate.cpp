@@ -136,7 +136,8 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
                                  const int32_t* block_tables, const int32_t* context_lens, int B,
                                  int Hq, int Hkv, int D, int BS, int MBS, int64_t NB, float scale,
                                  int kv_dtype, int partition_size, int window, int n_query,
-                                 const float* gamma_q, const float* gamma_k, float eps,
+                                 int prefix_blocks, const float* gamma_q, const float* gamma_k,
+                                 float eps,
                                  float rope_theta, const float* part_out, const float* part_max,
                                  const float* part_sum, const uint32_t* counters,
                                  int max_partitions) {
@@ -158,11 +159,28 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
   if (window > 0 && partition_size != 0) return PKV_EUNSUPPORTED;  // balanced split only
   if (n_query < 1) return PKV_EINVAL;
   if (n_query > 1) {
-    // several new tokens: balanced split, (Hq / Hkv) * n_query <= 16 columns,
-    // neither QK-norm nor a window
-    if (partition_size != 0 || window != 0 || gamma_k != nullptr) return PKV_EUNSUPPORTED;
+    // several new tokens: balanced split, no window.  Their (Hq / Hkv) *
+    // n_query query columns fill one 16-wide product (a power of two up to
+    // 16; with QK-norm up to 8) or whole 16-column groups, which take their
+    // new rows already appended (k_new == NULL, no QK-norm)
+    if (partition_size != 0 || window != 0) return PKV_EUNSUPPORTED;
+    if (n_query > pkv::kMaxNewTokens) return PKV_EUNSUPPORTED;
     const int cols = (Hq / Hkv) * n_query;
-    if (cols > 16 || (cols & (cols - 1)) != 0) return PKV_EUNSUPPORTED;
+    if (gamma_k != nullptr && cols > pkv::kQkNormCols) return PKV_EUNSUPPORTED;
+    if (cols <= pkv::kColsPerProduct) {
+      if ((cols & (cols - 1)) != 0) return PKV_EUNSUPPORTED;
+    } else {
+      if (cols % pkv::kColsPerProduct != 0 || k_new != nullptr) return PKV_EUNSUPPORTED;
+    }
+  }
+  if (prefix_blocks < 0 || prefix_blocks > MBS) return PKV_EINVAL;
+  if (prefix_blocks > 0) {
+    // the shared-prefix step: balanced split, one new token, no window or
+    // QK-norm; a (sequence, kv head) takes up to max_partitions / 2 prefix
+    // and own pieces each
+    if (partition_size != 0 || n_query != 1 || window != 0 || gamma_k != nullptr)
+      return PKV_EUNSUPPORTED;
+    if (max_partitions < 6) return PKV_EINVAL;
   }
   if (B == 0) return st;
   if (!out || !aligned(out, 16)) return PKV_EINVAL;

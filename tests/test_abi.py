@@ -178,7 +178,8 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 def _step_args(**kw):
     a = dict(out=A, q=A, k_new=A, v_new=A, k_pool=A, v_pool=A, k_scale=None, v_scale=None,
              block_tables=A, context_lens=A, B=2, Hq=8, Hkv=2, D=128, BS=16, MBS=8, NB=100,
-             scale=0.1, kv_dtype=0, partition_size=64, window=0, n_query=1, gamma_q=None,
+             scale=0.1, kv_dtype=0, partition_size=64, window=0, n_query=1, prefix_blocks=0,
+             gamma_q=None,
              gamma_k=None,
              eps=1e-6,
              theta=1e6, part_out=A, part_max=A, part_sum=A, counters=A, max_partitions=2)
@@ -199,9 +200,15 @@ def _step_args(**kw):
     (dict(n_query=2), -2),
     (dict(partition_size=0, max_partitions=16, n_query=4), 0),
     (dict(partition_size=0, max_partitions=16, n_query=3), -2),
-    (dict(partition_size=0, max_partitions=16, n_query=8), -2),
+    (dict(partition_size=0, max_partitions=16, n_query=8), -2),   # 32 columns: no in-launch append
+    (dict(partition_size=0, max_partitions=16, n_query=8, k_new=None, v_new=None), 0),
+    (dict(partition_size=0, max_partitions=16, n_query=512, k_new=None, v_new=None), 0),
+    (dict(partition_size=0, max_partitions=16, n_query=6, k_new=None, v_new=None), -2),
+    (dict(partition_size=0, max_partitions=16, n_query=8192, k_new=None, v_new=None), -2),
+    (dict(partition_size=512, n_query=8, k_new=None, v_new=None), -2),
     (dict(partition_size=0, max_partitions=16, n_query=2, window=64), -2),
-    (dict(partition_size=0, max_partitions=16, n_query=2, gamma_k=A, gamma_q=A), -2),
+    (dict(partition_size=0, max_partitions=16, n_query=2, gamma_k=A, gamma_q=A), 0),
+    (dict(partition_size=0, max_partitions=16, n_query=4, gamma_k=A, gamma_q=A), -2),
     (dict(partition_size=0, max_partitions=2), -1),
     (dict(partition_size=0, max_partitions=65), -2),
     (dict(partition_size=0, part_out=None), -1),
@@ -235,6 +242,17 @@ def _step_args(**kw):
     # ... which fixed partitions of 16 tokens could not launch
     (dict(partition_size=16, max_partitions=8192, B=512, Hq=64, Hkv=8, MBS=8192, NB=10 ** 6), -2),
     (dict(partition_size=0, max_partitions=16, part_max=None), -1),
+    (dict(partition_size=0, max_partitions=16, prefix_blocks=4), 0),
+    (dict(partition_size=0, max_partitions=16, prefix_blocks=8), 0),       # = MBS
+    (dict(partition_size=0, max_partitions=16, prefix_blocks=9), -1),      # > MBS
+    (dict(partition_size=0, max_partitions=16, prefix_blocks=-1), -1),
+    (dict(partition_size=0, max_partitions=5, prefix_blocks=4), -1),
+    (dict(prefix_blocks=4), -2),                                            # fixed partitions
+    (dict(partition_size=0, max_partitions=16, prefix_blocks=4, n_query=2), -2),
+    (dict(partition_size=0, max_partitions=16, prefix_blocks=4, window=64), -2),
+    (dict(partition_size=0, max_partitions=16, prefix_blocks=4, gamma_k=A, gamma_q=A), -2),
+    (dict(partition_size=0, max_partitions=16, prefix_blocks=4, kv_dtype=1, k_scale=A,
+          v_scale=A, k_new=None, v_new=None), 0),
     (dict(partition_size=0, max_partitions=16, part_sum=A + 2), -1),
 ])
 def test_step_validation_codes(lib, kw, code):
@@ -311,6 +329,8 @@ def test_static_step_partitions(lib):
     assert f(4096, 64, 8, 128, 16, 8, 1, 0) == -4               # partials do not fit
     assert f(40000, 8, 8, 128, 16, 8, 1, 0) == -4               # counters do not fit
     assert f(-1, 8, 8, 128, 16, 8, 1, 0) == -1
+    assert f(2, 32, 8, 128, 16, 40, 8, 0) == 16                  # 32 query columns, 2 groups
+    assert f(32, 32, 8, 128, 16, 80, 512, 0) == -4              # a 512-token chunk's partials
     per_slot = 256 * 32 * 130 * 4
     assert 7 * per_slot <= (31 << 20) < 8 * per_slot
 
