@@ -128,12 +128,39 @@ def _oracle_worker(seqs):
     return len(seqs)
 
 
+def single_core(cfg, d, budget_s):
+    """The oracle on one core (one thread): whole sequences of the batch in
+    order (again from the first after the last) until about budget_s of
+    work, at least one."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attn_ref
+
+    lens = d["context_lens"].astype(np.int64)
+    done, tokens, t0 = 0, 0, time.perf_counter()
+    with threadpool_limits(1):
+        while done == 0 or time.perf_counter() - t0 < budget_s:
+            b = done % cfg.B
+            attn_ref(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                     cfg.scale, k_scale=d["k_scale"], v_scale=d["v_scale"], seqs=[b])
+            tokens += int(lens[b])
+            done += 1
+    dt = time.perf_counter() - t0
+    kv = synth.kv_bytes(cfg, [tokens])
+    return {"config": cfg.name, "value": kv / dt / 1e9, "unit": "GB/s", "cores": 1,
+            "sample": f"{done} sequences of the {cfg.B}-sequence batch in order, one thread",
+            "seconds": dt, "step_seconds_extrapolated": dt * float(lens.sum()) / tokens}
+
+
 def cpu_baseline(cfg, d, budget_s):
     """Time the fp64 oracle on a bounded sample of the batch, parallel over
-    sequences with one single-threaded worker per host core (fork, before
-    the GPU is touched)."""
+    sequences with one single-threaded worker per host core of the box's
+    share (fork, before the GPU is touched), and on one core for this
+    config and the tiny config."""
     import multiprocessing as mp
 
+    # the GPU box allots 16 host cores to one GPU, whatever the affinity
+    # mask shows: the pool never has more workers than that
     cores = min(len(os.sched_getaffinity(0)), 16)
     _CPU.update(d=d, cfg=cfg)
     lens = d["context_lens"].astype(np.int64)
@@ -166,6 +193,10 @@ def cpu_baseline(cfg, d, budget_s):
         "seconds": dt,
         "step_seconds_extrapolated": dt / frac,
         "cpu_model": _cpu_model(),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+        "single_core": [single_core(cfg, d, budget_s / 4)] + (
+            [] if cfg.name == "c1" else
+            [single_core(synth.CONFIGS["c1"], synth.generate(synth.CONFIGS["c1"]), 0.5)]),
     }
 
 
