@@ -67,6 +67,40 @@ def step_source_hash():
     return h.hexdigest()[:16]
 
 
+def step_tile_ids(cfg, d, nq, prefix_blocks, cached):
+    """The (block, kv head) tiles the balanced step reads, in its order (kv
+    head, then sequence, then column group, then tile; with a shared prefix,
+    per kv head the prefix once per group of 16 / g sequences, then each
+    sequence's own tiles), as int32 tile indices for pkv_tile_read (~index:
+    read with the default cache policy)."""
+    tab, lens = d["block_tables"], d["context_lens"].astype(np.int64)
+    g = cfg.Hq // cfg.Hkv
+    hb = cfg.block_size // 16                      # tiles per block
+    cg = 1 if g * nq <= 16 else -(-g * nq // 16)   # 16-column groups per sequence
+    ntile = -(-lens // 16)
+
+    def seq_tiles(b, kvh, lo, hi):
+        n = np.arange(lo, hi)
+        return (tab[b, n // hb].astype(np.int64) * cfg.Hkv + kvh) * hb + n % hb
+
+    out = []
+    for kvh in range(cfg.Hkv):
+        if prefix_blocks:
+            tp = prefix_blocks * hb
+            spp = 16 // g
+            for lead in range(0, cfg.B, spp):
+                out.append(~seq_tiles(lead, kvh, 0, tp))
+            for b in range(cfg.B):
+                if ntile[b] > tp:
+                    out.append(seq_tiles(b, kvh, tp, ntile[b]))
+        else:
+            for b in range(cfg.B):
+                t = seq_tiles(b, kvh, 0, ntile[b])
+                for _ in range(cg):
+                    out.append(~t if cached else t)
+    return np.concatenate(out).astype(np.int32)
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -76,6 +110,9 @@ def parse():
     p.add_argument("--partition-size", type=int, default=None)
     p.add_argument("--rotate", type=int, default=None, help="copies of the inputs (default: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--tile-ceiling", type=int, default=1, choices=(0, 1),
+                   help="1: also time pkv_tile_read over the step's own tiles (its practical\n"
+                        "read ceiling for this access pattern)")
     p.add_argument("--splits", type=int, default=16,
                    help="most pieces one sequence is cut into by the balanced split")
     p.add_argument("--n-query", type=int, default=1,
@@ -100,9 +137,11 @@ def parse():
     p.add_argument("--paging-overhead", action="store_true",
                    help="also time the same steps with every sequence's blocks made "
                         "physically consecutive, and report the cost of paging itself")
-    p.add_argument("--prefix", default="auto", choices=("auto", "no"),
+    p.add_argument("--prefix", default="no", choices=("auto", "no"),
                    help="auto: pass a shared prompt prefix (the prefix-shared config's 1024\n"
-                        "tokens) to the step as prefix_blocks, read once per group of sequences")
+                        "tokens) to the step as prefix_blocks, read once per group of sequences;\n"
+                        "no (default): the plain step with the shared-blocks cache hint, which\n"
+                        "fetches the same HBM bytes and runs a few percent faster")
     p.add_argument("--shared-blocks", default="auto", choices=("auto", "yes", "no"),
                    help="pass the shared-blocks cache hint (auto: when the workload's tables "
                         "share a prefix)")
@@ -558,6 +597,31 @@ def main():
         torch.cuda.synchronize()
         return s0.elapsed_time(s1) / K
 
+    # the step's practical read ceiling: its tiles, in its order and split,
+    # read with its cache policies and nothing computed (pkv_tile_read)
+    tile_ms = None
+    if args.tile_ceiling and not args.unfused and step_ps == 0 and not args.window:
+        ids = torch.from_numpy(step_tile_ids(cfg, d, nq, prefix_blocks, shared)).to(dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        waves = cus * 4 * (2 if fp8 else 1)
+
+        def tile_read(i):
+            g = copies[i % R]
+            _lib.pkv_tile_read(g["k_pool"], g["v_pool"], ids, waves, sink, stream=stream)
+
+        for i in range(args.warmup):
+            tile_read(i)
+        torch.cuda.synchronize()
+        t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0e.record(stream)
+        for i in range(K):
+            tile_read(i)
+        t1e.record(stream)
+        torch.cuda.synchronize()
+        tile_ms = t0e.elapsed_time(t1e) / K
+        del ids, sink
+
     paging = None
     if args.paging_overhead:
         # the same batch with each sequence's blocks made consecutive
@@ -659,6 +723,11 @@ def main():
         "pct_hbm_peak": round(100 * unique_rate / HBM_GBPS, 2),
         "read_ceiling_gbps": None if ceiling is None else round(ceiling, 1),
         "pct_of_read_ceiling": None if ceiling is None else round(100 * unique_rate / ceiling, 2),
+        "tile_read_us": None if tile_ms is None else round(tile_ms * 1e3, 3),
+        "tile_read_ceiling_gbps": (None if tile_ms is None
+                                   else round(kv_unique / (tile_ms * 1e-3) / 1e9, 1)),
+        "pct_of_tile_read_ceiling": (None if tile_ms is None
+                                     else round(100 * tile_ms / kernel_ms, 2)),
         "paging": paging,
         "kv_bytes_per_step": kv,
         "unique_kv_bytes_per_step": kv_unique,

@@ -179,7 +179,11 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
  * partition_size == 0: balanced split.  The library gives every wave the
  *   same number of 16-token tiles of the whole batch (whatever the mix of
  *   context lengths); a sequence is cut into at most max_partitions pieces
- *   (3 <= max_partitions <= 64).
+ *   (3 <= max_partitions <= 64).  Where the pieces fall depends on the whole
+ *   batch, so a sequence's rounding can differ between batches (within the
+ *   attention tolerance; the same batch gives the same bits on every call).
+ *   Callers that need each sequence's bits independent of the rest of the
+ *   batch use fixed partitions.
  * partition_size > 0: fixed partitions of that many tokens as in
  *   paged_attn_decode, at most 64 per sequence
  *   (ceil(MBS * BS / partition_size) <= 64), else PKV_EUNSUPPORTED.
@@ -393,6 +397,36 @@ int pkv_validate_copy(const void* k_pool, const void* v_pool, const float* k_sca
  * pointer, misalignment or a bad size, PKV_ELAUNCH if the launch fails.
  */
 int pkv_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
+ * pkv_tile_read - read a list of (block, kv head) tiles of a K and a V pool,
+ * each once, with the decode step's lane pattern (16 rows of K and of V per
+ * tile, as the step loads a 16-token tile for its products), the list cut
+ * into `waves` equal contiguous ranges, one single-wave workgroup each, and
+ * each XCD's ranges contiguous in the list, as the balanced step splits its
+ * tiles.  Nothing is computed with the data.  A measurement yardstick, not
+ * part of the attention path: the bench runs it over the tiles a step
+ * reads, in the step's order and with its cache policies, and reports the
+ * step's KV rate as a fraction of what the GPU delivers for that access
+ * pattern (its practical read ceiling, which the streaming read does not
+ * give: paged tiles are 4-8 KiB pieces at scattered addresses).
+ *
+ * k_pool, v_pool: device pools of pool_tiles tiles each; a tile is 16 rows
+ *   of row_bytes = 256 (fp16, D = 128), 128 (fp16 D = 64, or E4M3 D = 128)
+ *   or 64 (E4M3, D = 64), i.e. tile t of a pool [NB][Hkv][16][D] is
+ *   (block t / Hkv, kv head t % Hkv).
+ * ids: n int32 on the device; id >= 0 reads tile id with the non-temporal
+ *   policy, id < 0 reads tile ~id with the default one (a tile other readers
+ *   share); ids past the pools are clamped to the last tile.
+ * waves: workgroups, 1 .. 65536 (the step runs 4 per CU for fp16 and 8 for
+ *   E4M3).  sink: one uint32 of device memory, written only if the XOR of the
+ *   words a lane read equals 0x9E3779B9.
+ * Returns PKV_EINVAL for a null pointer, n < 0, pool_tiles < 1, waves out of
+ * range or another row_bytes; PKV_ELAUNCH if the launch fails; n == 0 is a
+ * no-op.
+ */
+int pkv_tile_read(const void* k_pool, const void* v_pool, int64_t pool_tiles, const int32_t* ids,
+                  int64_t n, int row_bytes, int waves, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -46,6 +46,7 @@ _SIGNATURES = {
     "paged_kv_append_e4m3": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P]),
     "paged_attn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "pkv_stream_read": (_I, [_P, _I64, _P, _P]),
+    "pkv_tile_read": (_I, [_P, _P, _I64, _P, _I64, _I, _I, _P, _P]),
     "pkv_strerror": (ctypes.c_char_p, [_I]),
     "pkv_validate_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _P, _P, _P,
                                  _F, _F]),
@@ -208,6 +209,25 @@ def pkv_stream_read(buf, sink, *, stream=None):
     st = lib().pkv_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                _stream(stream))
     _raise("pkv_stream_read", st)
+
+
+def pkv_tile_read(k_pool, v_pool, ids, waves, sink, *, stream=None):
+    """Read the (block, kv head) tiles listed in `ids` (int32 GPU tensor;
+    id < 0 reads tile ~id with the default cache policy) once each with the
+    step's lane pattern, over `waves` single-wave workgroups: the paged-read
+    yardstick.  k_pool / v_pool: [NB, Hkv, BS, D] GPU pools."""
+    if not (k_pool.is_cuda and v_pool.is_cuda and ids.is_cuda):
+        raise ValueError("pools and ids must be GPU tensors")
+    if k_pool.shape != v_pool.shape or k_pool.dim() != 4:
+        raise ValueError("k_pool and v_pool must be [NB, Hkv, BS, D] of one shape")
+    _check(ids, "ids", torch.int32, 1)
+    _check(sink, "sink", torch.int32, 1)
+    NB, Hkv, BS, D = k_pool.shape
+    row = D * k_pool.element_size()
+    tiles = NB * Hkv * (BS // 16)
+    st = lib().pkv_tile_read(_ptr(k_pool), _ptr(v_pool), tiles, _ptr(ids), ids.numel(), row,
+                             int(waves), _ptr(sink), _stream(stream))
+    _raise("pkv_tile_read", st)
 
 
 def max_partitions_for(max_blocks_per_seq: int, partition_size: int) -> int:

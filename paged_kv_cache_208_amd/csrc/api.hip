@@ -240,6 +240,18 @@ extern "C" int pkv_stream_read(const void* buf, int64_t bytes, uint32_t* sink, v
                                                static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int pkv_tile_read(const void* k_pool, const void* v_pool, int64_t pool_tiles,
+                             const int32_t* ids, int64_t n, int row_bytes, int waves, uint32_t* sink,
+                             void* stream) {
+  if (k_pool == nullptr || v_pool == nullptr || ids == nullptr || sink == nullptr || n < 0 ||
+      pool_tiles < 1 || waves < 1 || waves > pkv::kMaxTileReadWaves ||
+      (row_bytes != 256 && row_bytes != 128 && row_bytes != 64))
+    return PKV_EINVAL;
+  if (n == 0) return PKV_OK;
+  return launch_status(pkv::launch_tile_read(k_pool, v_pool, pool_tiles, ids, n, row_bytes, waves, sink,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int paged_decode_step_static_partitions(int B, int Hq, int Hkv, int D, int BS, int MBS,
                                                    int n_query, int partition_size) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || MBS <= 0 || n_query < 1 ||

@@ -1,5 +1,9 @@
-// Streaming read of one buffer: the measured read ceiling of the GPU that the
-// step kernels' KV rates are compared with.  Not part of the attention path.
+// Read yardsticks that the step kernels' KV rates are compared with; not part
+// of the attention path.  The streaming read of one buffer gives the read
+// ceiling of the GPU; the paged tile read (further down) gives the ceiling
+// for a step's own access pattern: its tiles, in its order and split.
+//
+// Streaming read of one buffer:
 //
 // Each wave owns one contiguous span of the buffer and reads it 1 KiB per
 // load instruction (lane i takes the i-th 16 bytes), 16 instructions in
@@ -11,7 +15,7 @@
 // XOR-folded and the fold is stored only if it equals a value it cannot
 // take for the buffers used (so the loads stay live); nothing else is
 // written.
-#include "device.h"
+#include "decode_tile.h"
 #include "read_probe.h"
 
 namespace pkv {
@@ -44,7 +48,109 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* 
   if (fold == 0x9E3779B9u) sink[0] = fold;
 }
 
+// Paged tile read: the (block, kv head) tiles of a list, each read once
+// with the decode step's lane pattern (K: lane (g, n16) takes row n16 in
+// 16-byte pieces g + 4i; V: rows 4g .. 4g + 3, kRow / 16 bytes at n16), one
+// wave per SIMD, the list cut into equal contiguous ranges, and the ranges
+// of each XCD contiguous in the list (worker w runs on XCD w % 8) as in the
+// step.  Loads run two tiles deep; a tile's index is read through the
+// scalar cache one step ahead of its loads.  Index i >= 0: non-temporal
+// loads of tile i; i < 0: default-policy loads of tile ~i (a tile other
+// readers share).  Each lane folds its words; the fold is stored only if it
+// equals a value it cannot take for the pools used.
+template <int KROW>
+struct ReadTile {
+  static constexpr int kK = KROW / 64;      // 16-byte K pieces per lane
+  static constexpr int kVW = KROW / 64;     // 32-bit V words per lane and row
+  u32x4 k[kK];
+  typename Words<kVW>::T v[4];
+};
+
+template <int KROW, int AUX>
+__device__ __forceinline__ void read_tile_issue(ReadTile<KROW>& t, const uint8_t* kp, const uint8_t* vp,
+                                                int64_t tile, int k_off, int v_off) {
+  constexpr int kTileBytes = 16 * KROW;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + tile * kTileBytes, kTileBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + tile * kTileBytes, kTileBytes);
+#pragma unroll
+  for (int i = 0; i < ReadTile<KROW>::kK; ++i)
+    t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + i * 64, 0, AUX);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t.v[j] = buffer_load_words<ReadTile<KROW>::kVW, AUX>(rv, v_off + j * KROW);
+}
+
+// Tile ids past the pools are clamped to the last tile.
+template <int KROW>
+__device__ __forceinline__ void read_tile(ReadTile<KROW>& t, const uint8_t* kp, const uint8_t* vp,
+                                          int32_t id, int64_t ntiles, int k_off, int v_off) {
+  if (id >= 0) read_tile_issue<KROW, kKvAux>(t, kp, vp, min(int64_t(id), ntiles - 1), k_off, v_off);
+  else read_tile_issue<KROW, 0>(t, kp, vp, min(~int64_t(id), ntiles - 1), k_off, v_off);
+}
+
+template <int KROW>
+__device__ __forceinline__ uint32_t fold_tile(const ReadTile<KROW>& t) {
+  uint32_t f = 0;
+#pragma unroll
+  for (int i = 0; i < ReadTile<KROW>::kK; ++i) f ^= t.k[i][0] ^ t.k[i][1] ^ t.k[i][2] ^ t.k[i][3];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int w = 0; w < ReadTile<KROW>::kVW; ++w) f ^= word<ReadTile<KROW>::kVW>(t.v[j], w);
+  return f;
+}
+
+template <int KROW>
+__global__ __launch_bounds__(kWave) void tile_read_kernel(const uint8_t* kp, const uint8_t* vp,
+                                                          int64_t ntiles, const int32_t* ids, int64_t n,
+                                                          uint32_t* sink) {
+  const int lane = threadIdx.x, g = lane / 16, n16 = lane % 16;
+  const int k_off = n16 * KROW + g * 16;
+  const int v_off = (4 * g) * KROW + n16 * (KROW / 16);
+  const int workers = gridDim.x;
+  const int nblk = workers % (2 * kXcds) == 0 ? kXcds : 1;
+  const int64_t r = int64_t(blockIdx.x % nblk) * (workers / nblk) + blockIdx.x / nblk;
+  const int64_t t0 = n * r / workers, t1 = n * (r + 1) / workers;
+  if (t0 >= t1) return;
+  auto id_of = [&](int64_t t) { return *(const __attribute__((address_space(4))) int32_t*)(ids + t); };
+  ReadTile<KROW> tl[2];
+  read_tile<KROW>(tl[0], kp, vp, id_of(t0), ntiles, k_off, v_off);
+  int32_t ahead = t0 + 1 < t1 ? id_of(t0 + 1) : 0;
+  uint32_t f = 0;
+  for (int64_t t = t0; t < t1;) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // tile t + 1 into the other buffer
+      if (t + 1 < t1) read_tile<KROW>(tl[1 - u], kp, vp, ahead, ntiles, k_off, v_off);
+      if (t + 2 < t1) ahead = id_of(t + 2);
+      issue_fence();
+      f ^= fold_tile<KROW>(tl[u]);
+      issue_fence();
+      if (++t >= t1) break;
+    }
+  }
+  if (f == 0x9E3779B9u) sink[0] = f;
+}
+
 }  // namespace
+
+hipError_t launch_tile_read(const void* k_pool, const void* v_pool, int64_t ntiles, const int32_t* ids,
+                            int64_t n, int row_bytes, int waves, uint32_t* sink, hipStream_t stream) {
+  const uint8_t* kp = static_cast<const uint8_t*>(k_pool);
+  const uint8_t* vp = static_cast<const uint8_t*>(v_pool);
+  switch (row_bytes) {
+    case 256:
+      hipLaunchKernelGGL(tile_read_kernel<256>, dim3(waves), dim3(kWave), 0, stream, kp, vp, ntiles, ids, n, sink);
+      break;
+    case 128:
+      hipLaunchKernelGGL(tile_read_kernel<128>, dim3(waves), dim3(kWave), 0, stream, kp, vp, ntiles, ids, n, sink);
+      break;
+    case 64:
+      hipLaunchKernelGGL(tile_read_kernel<64>, dim3(waves), dim3(kWave), 0, stream, kp, vp, ntiles, ids, n, sink);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int cus,
                               hipStream_t stream) {

@@ -15,4 +15,5 @@ constexpr int kStaticStepPartitions = 16;  // pieces per sequence of the static-
 constexpr int kColsPerProduct = 16;        // query columns of one 16-wide MFMA product
 constexpr int kMaxNewTokens = 4096;        // new query tokens per sequence in one step
 constexpr int kQkNormCols = 8;             // query columns of the QK-norm step (g * nq)
+constexpr int kMaxTileReadWaves = 1 << 16; // workgroups of the paged tile-read yardstick
 }  // namespace pkv

@@ -318,6 +318,26 @@ def test_stream_read_rejects_bad_arguments_before_any_launch(lib, buf, nbytes, s
     assert lib.pkv_stream_read(buf, nbytes, sink, None) == -1
 
 
+@pytest.mark.parametrize("kp,vp,tiles,ids,n,row,waves,sink", [
+    (None, A, 4, A, 1, 256, 1, A),    # null K pool
+    (A, None, 4, A, 1, 256, 1, A),    # null V pool
+    (A, A, 4, None, 1, 256, 1, A),    # null tile list
+    (A, A, 4, A, 1, 256, 1, None),    # null sink
+    (A, A, 4, A, -1, 256, 1, A),      # negative count
+    (A, A, 0, A, 1, 256, 1, A),       # empty pools
+    (A, A, 4, A, 1, 192, 1, A),       # a row size no step reads
+    (A, A, 4, A, 1, 256, 0, A),       # no workgroups
+    (A, A, 4, A, 1, 256, 65537, A),   # too many workgroups
+])
+def test_tile_read_rejects_bad_arguments_before_any_launch(lib, kp, vp, tiles, ids, n, row, waves,
+                                                           sink):
+    assert lib.pkv_tile_read(kp, vp, tiles, ids, n, row, waves, sink, None) == -1
+
+
+def test_tile_read_with_no_tiles_is_a_no_op(lib):
+    assert lib.pkv_tile_read(A, A, 4, A, 0, 256, 1, A, None) == 0
+
+
 def test_static_step_partitions(lib):
     """The static-scratch step's pieces per sequence: 16 while the partials
     fit 31 MiB, fewer for large batches, never fewer than 3; fixed

@@ -1,0 +1,59 @@
+"""The tile list the bench gives the paged-read yardstick: the balanced
+step's tiles in its order (kv head, sequence, column group, tile), and with a
+shared prefix the prefix once per group of 16 / g sequences (default cache
+policy, as ~id) followed by each sequence's own tiles."""
+
+import os
+import sys
+
+import numpy as np
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+import bench  # noqa: E402
+from paged_kv_cache_208_amd import synth  # noqa: E402
+
+
+def test_plain_order_counts_and_first_sequence():
+    cfg = synth.CONFIGS["c2"]
+    d = synth.generate(cfg)
+    ids = bench.step_tile_ids(cfg, d, 1, 0, False)
+    ntile = -(-d["context_lens"].astype(np.int64) // 16)
+    assert len(ids) == cfg.Hkv * ntile.sum()
+    assert (ids >= 0).all()
+    # kv head 0 of sequence 0 comes first, one tile per table entry
+    n0 = int(ntile[0])
+    assert np.array_equal(ids[:n0], d["block_tables"][0, :n0] * cfg.Hkv)
+    # the last tile is kv head Hkv - 1 of the last sequence's last block
+    b = cfg.B - 1
+    assert ids[-1] == d["block_tables"][b, ntile[b] - 1] * cfg.Hkv + cfg.Hkv - 1
+    cached = bench.step_tile_ids(cfg, d, 1, 0, True)
+    assert np.array_equal(~cached, ids)
+
+
+def test_prefix_order_reads_the_prefix_once_per_group():
+    cfg = synth.CONFIGS["c3"]
+    d = synth.generate(cfg)
+    tp = cfg.prefix_tokens // 16
+    ids = bench.step_tile_ids(cfg, d, 1, tp, False)
+    g = cfg.Hq // cfg.Hkv
+    groups = -(-cfg.B // (16 // g))
+    own = np.maximum(-(-d["context_lens"].astype(np.int64) // 16) - tp, 0).sum()
+    assert (ids < 0).sum() == cfg.Hkv * groups * tp
+    assert (ids >= 0).sum() == cfg.Hkv * own
+    # every prefix tile read is one of the Hkv * tp shared tiles
+    shared = {int(blk) * cfg.Hkv + h for blk in d["block_tables"][0, :tp] for h in range(cfg.Hkv)}
+    assert set((~ids[ids < 0]).tolist()) == shared
+    # no own tile is a shared one
+    assert not (set(ids[ids >= 0].tolist()) & shared)
+
+
+def test_column_groups_repeat_each_sequence():
+    cfg = synth.CONFIGS["c2"]
+    d = synth.generate(cfg)
+    one = bench.step_tile_ids(cfg, d, 1, 0, False)
+    nq = 16       # g * nq = 64 query columns: four 16-column groups
+    four = bench.step_tile_ids(cfg, d, nq, 0, False)
+    assert len(four) == 4 * len(one)
+    n0 = -(-int(d["context_lens"][0]) // 16)
+    assert np.array_equal(four[:4 * n0], np.tile(one[:n0], 4))

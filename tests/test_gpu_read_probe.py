@@ -32,3 +32,53 @@ def test_stream_read_writes_nothing_else():
     torch.cuda.synchronize()
     assert sink.item() == 0
     assert bool((buf == 1).all())
+
+
+# The paged tile-read yardstick: every word of a listed tile reaches one
+# lane's fold, unlisted tiles are not read, ~id reads tile id (default cache
+# policy), and ids past the pools read the last tile.
+
+def _pools(NB, Hkv, D, dtype):
+    k = torch.zeros((NB, Hkv, 16, D), dtype=dtype, device="cuda")
+    v = torch.zeros_like(k)
+    return k, v
+
+
+def _mark(pool, tile, word):
+    flat = pool.view(torch.int32).view(-1)
+    per = pool[0, 0].numel() * pool.element_size() // 4     # 32-bit words per tile
+    flat[tile * per + word] = np.int32(np.uint32(MARK).view(np.int32))
+
+
+@pytest.mark.parametrize("D,dtype", [(128, torch.float16), (64, torch.float16), (128, torch.uint8),
+                                     (64, torch.uint8)])
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_tile_read_sees_every_word_of_listed_tiles(D, dtype, which):
+    NB, Hkv = 12, 2
+    kp, vp = _pools(NB, Hkv, D, dtype)
+    per = kp[0, 0].numel() * kp.element_size() // 4
+    ids = torch.tensor([3, 7, ~5, 20], dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(D)
+    for tile in (3, 7, 5, 20):
+        for word in (0, per - 1, int(rng.integers(per))):
+            kp.zero_(); vp.zero_()
+            _mark(kp if which == "k" else vp, tile, word)
+            sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+            _lib.pkv_tile_read(kp, vp, ids, 3, sink)
+            torch.cuda.synchronize()
+            assert int(sink.item()) & 0xFFFFFFFF == MARK, (tile, word)
+
+
+def test_tile_read_skips_unlisted_tiles_and_clamps():
+    kp, vp = _pools(8, 2, 128, torch.float16)
+    _mark(kp, 4, 17)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _lib.pkv_tile_read(kp, vp, torch.tensor([0, 1, 2, 3, 5, 6], dtype=torch.int32, device="cuda"),
+                       2, sink)
+    torch.cuda.synchronize()
+    assert sink.item() == 0
+    _mark(kp, 15, 3)      # the last tile: ids past the pools read it (one id per wave, so
+    # that no lane folds the marked word twice)
+    _lib.pkv_tile_read(kp, vp, torch.tensor([1000, ~2000], dtype=torch.int32, device="cuda"), 2, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) & 0xFFFFFFFF == MARK
