@@ -137,11 +137,11 @@ def parse():
     p.add_argument("--paging-overhead", action="store_true",
                    help="also time the same steps with every sequence's blocks made "
                         "physically consecutive, and report the cost of paging itself")
-    p.add_argument("--prefix", default="no", choices=("auto", "no"),
+    p.add_argument("--prefix", default="auto", choices=("auto", "no"),
                    help="auto: pass a shared prompt prefix (the prefix-shared config's 1024\n"
-                        "tokens) to the step as prefix_blocks, read once per group of sequences;\n"
-                        "no (default): the plain step with the shared-blocks cache hint, which\n"
-                        "fetches the same HBM bytes and runs a few percent faster")
+                        "tokens) to the step as prefix_blocks, read once per group of sequences\n"
+                        "(attend, then a combine launch); no: the plain one-launch step with the\n"
+                        "shared-blocks cache hint")
     p.add_argument("--shared-blocks", default="auto", choices=("auto", "yes", "no"),
                    help="pass the shared-blocks cache hint (auto: when the workload's tables "
                         "share a prefix)")
@@ -710,7 +710,7 @@ def main():
                      ("qknorm_rope+append+attend+combine" if cfg.fused_append
                       else "append+attend+combine")),
             "launches_per_step": ((3 if not fp8 else 2) if args.unfused and PS
-                                  else 2 if chunk and not fp8 else 1),
+                                  else 2 if (chunk and not fp8) or prefix_blocks else 1),
             "window": args.window,
             "new_tokens_per_sequence": nq,
             "shared_prefix_blocks": prefix_blocks,

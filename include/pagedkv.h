@@ -160,10 +160,11 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
                       int D, int partition_size, int max_partitions, void* stream);
 
 /*
- * paged_decode_step - one whole decode step in one launch: the three calls
- * above fused, for the common case where each sequence's new token is its
- * last one ("Distributed LLM Inference Serving Platform", section 5.1: write
- * the new token's K/V into its block, then attend over the block table).
+ * paged_decode_step - one whole decode step, enqueued on `stream` in one or
+ * two launches: the three calls above fused, for the common case where each
+ * sequence's new token is its last one ("Distributed LLM Inference Serving
+ * Platform", section 5.1: write the new token's K/V into its block, then
+ * attend over the block table).
  * For every sequence b with L_b = context_lens[b] >= 1:
  *  1. if k_new != NULL, k_new[b] and v_new[b] ([B][Hkv][D] fp16) become token
  *     L_b - 1: they are written to block block_tables[b][(L_b-1)/BS], row
@@ -173,9 +174,16 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
  *     rewritten in place, exactly as paged_kv_append does;
  *  2. q attends over the sequence's paged KV as in paged_attn_decode;
  *  3. each sequence's context is split into pieces that different
- *     workgroups read in parallel, and the last piece to finish for each
- *     (sequence, kv head) combines them as paged_attn_reduce does, so out
- *     [B][Hq][D] fp16 is complete when the launch is.
+ *     workgroups read in parallel, and the pieces of each (sequence, kv
+ *     head) are combined as paged_attn_reduce does, so out [B][Hq][D] fp16
+ *     is complete when the step's last launch is.  Balanced split: a
+ *     (sequence, kv head) that one workgroup reads whole is written by it
+ *     directly; the others are combined by a second launch (their first
+ *     piece leaves the piece count in `counters`, which that launch reads
+ *     and clears), except with QK-norm, where the last piece to finish
+ *     combines them in the same launch (it also writes q' back, which must
+ *     wait until every piece has read q).  Fixed partitions: the last
+ *     partition to finish combines, in the one launch.
  * partition_size == 0: balanced split.  The library gives every wave the
  *   same number of 16-token tiles of the whole batch (whatever the mix of
  *   context lengths); a sequence is cut into at most max_partitions pieces
@@ -226,7 +234,10 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
  *   "Distributed LLM Inference Serving Platform", sections 2 and 11:
  *   reference-counted shared blocks).  Each prefix tile is then read once
  *   per group of 16 / (Hq / Hkv) sequences, whose q heads fill the columns
- *   of the same products, instead of once per sequence.  Device-data
+ *   of the same products, instead of once per sequence.  The step then
+ *   takes two launches on `stream`: the attention writes every piece's
+ *   partial and the piece counts (in `counters`), and a second launch
+ *   combines each (sequence, kv head) and clears its counter.  Device-data
  *   contract (not checked): those entries agree across the batch, and every
  *   sequence has L_b == 0 or L_b > prefix_blocks * BS (the prefix holds
  *   past tokens only, so the new row never lands in a shared block); a

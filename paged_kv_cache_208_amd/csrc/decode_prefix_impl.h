@@ -19,17 +19,20 @@
 // groups of the kv head read them next, on the same XCD), own tiles with
 // the non-temporal one.
 //
-// Arrival counting: a (sequence, kv head) expects np prefix pieces (known to
-// every wave from the range arithmetic) and no own pieces (known to the
-// waves holding its own tiles).  Every piece adds 1; the own segment's first
-// piece also adds 2^31 + no * 2^16, so the arrival that completes the count
-// sees bit 31 set and np + no arrivals in the low 16 bits, and takes no from
-// bits 16..30.  It combines the np + no partials (prefix pieces in slots
-// 0..np-1, own pieces in slots np..np+no-1) and re-arms the counter.
+// Every (sequence, kv head) output combines its group's np prefix pieces
+// and its own pieces (log-sum-exp, as paged_attn_reduce does), in a second
+// launch: with the combine in the same launch, the last piece of an output
+// to arrive would combine it, and the waves that finish last (those holding
+// the prefix spans of whole groups) would pile up the combines of every
+// member.  The attend launch writes each piece's partial (prefix pieces in
+// slots 0..np-1, own pieces after them); the own part's first piece also
+// stores np + (own pieces) in the output's counter, which the combine
+// launch reads, uses and clears (one wave per output).
 //
-// A segment that ends inside a wave's range publishes its partials and
-// arrives there (a full wait for the stores, then the counter); only the
-// range's last segment waits until the end.
+// A piece that ends inside a wave's range is parked in LDS and written out
+// with the range's last piece: a store issued between tile loads would hold
+// up the wait for every tile behind it (vector memory operations complete
+// in issue order).  A wave with more pieces than LDS slots writes early.
 #pragma once
 #include "decode_stream_impl.h"
 
@@ -250,13 +253,6 @@ struct PrefixKernel {
     }
   }
 
-  static __device__ __forceinline__ uint32_t arrive_add(const DecodeArgs& a, int seg, uint32_t add) {
-    uint32_t prev = 0;
-    if ((threadIdx.x & (kWave - 1)) == 0)
-      prev = __hip_atomic_fetch_add(a.counters + seg, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __builtin_amdgcn_readfirstlane(prev);
-  }
-
   // Pieces of the prefix span of group grp (kv head kvh).
   static __device__ __forceinline__ int prefix_pieces(const Ranges& rg, const PrefixGeom& pg, int kvh,
                                                       int grp) {
@@ -264,58 +260,73 @@ struct PrefixKernel {
     return int(rg.of(S + pg.Tp - 1) - rg.of(S) + 1);
   }
 
-  // A segment's piece of this wave's range ends: publish its partials, count
-  // the arrivals, and combine every (sequence, kv head) whose count is now
-  // complete.
-  static __device__ __forceinline__ void piece_end(const DecodeArgs& a, int B, const Meta& m,
-                                                   const MState<D, FP8>& st, const Ranges& rg,
-                                                   const PrefixGeom& pg, int64_t rw, int64_t t0,
-                                                   int64_t t1, int g, int n16, float* s_stage,
-                                                   float* s_w) {
+  // LDS slots for parked pieces: four for fp16 waves (one per SIMD), two
+  // for E4M3 waves (two per SIMD), so that a CU's waves fit in its LDS.
+  static constexpr int kSlots = FP8 ? 2 : 4;
+  // Row entries: at most kSpp per parked piece.
+  static constexpr int kEntries = kSlots * kSpp;
+
+  // Row entry e (3 ints in LDS): the (sequence, kv head) output, the piece
+  // count it stores in the output's counter (own part's first piece; else
+  // 0), and where the rows are: partial slot j in memory, member s of LDS
+  // slot k, kind (1: a prefix span's 16 staged columns, 0: an own piece's C).
+  static __device__ __forceinline__ void put_entry(int* s_ent, int e, int seg, int count, int j, int s,
+                                                   int kind, int k) {
+    s_ent[3 * e] = seg;
+    s_ent[3 * e + 1] = count;
+    s_ent[3 * e + 2] = j | (s << 8) | (kind << 16) | (k << 20);
+  }
+
+  // Park the partial of piece m (which ends in this range) in LDS slot k
+  // and append its row entries (every member with own tiles for a prefix
+  // span: the others have no output) to the nent so far; returns the new
+  // count.
+  static __device__ __forceinline__ int park(const DecodeArgs& a, int B, const Meta& m,
+                                             const MState<D, FP8>& st, const Ranges& rg,
+                                             const PrefixGeom& pg, int64_t rw, int64_t t0, int64_t t1,
+                                             int g, int n16, int k, float* s_stage, int* s_ent,
+                                             int nent) {
+    const int lane = threadIdx.x & (kWave - 1);
     const float l = group4_sum(st.l);
     const int64_t r_first = m.S >= t0 ? rw : rg.of(m.S);
     const int64_t r_last = m.S + m.T <= t1 ? rw : rg.of(m.S + m.T - 1);
     const int pieces = int(r_last - r_first + 1);
     const int j = int(rw - r_first);
+    float* s_k = s_stage + k * kStage;
     if (m.kind == 0) {
-      const int seg = m.b * a.Hkv + m.kvh;
       const int np = prefix_pieces(rg, pg, m.kvh, m.b / kSpp);
-      stage<C>(st, l, g, n16, s_stage);
-      write_rows(a, seg, np + j, s_stage, s_stage + C * D, s_stage + C * D + C);
-      __builtin_amdgcn_s_waitcnt(0);  // partials at device scope
-      const uint32_t add = j == 0 ? (1u << 31) | (uint32_t(pieces) << 16) | 1u : 1u;
-      complete(a, seg, np, arrive_add(a, seg, add) + add, s_w);
-    } else {
-      stage<16>(st, l, g, n16, s_stage);
-      uint32_t live = 0;  // members with own tiles (the others have no output to combine)
-#pragma unroll
-      for (int s = 0; s < kSpp; ++s) {
-        const int b = m.b + s;
-        const int Lb = load_uniform(a.context_lens + min(b, B - 1));  // in bounds either way
-        if (b < B && own_tiles(Lb, pg.Tp) > 0) {
-          live |= 1u << s;
-          write_rows(a, b * a.Hkv + m.kvh, j, s_stage + s * C * D, s_stage + 16 * D + s * C,
-                     s_stage + 16 * D + 16 + s * C);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      uint32_t after[kSpp];
-#pragma unroll
-      for (int s = 0; s < kSpp; ++s)
-        after[s] = (live >> s) & 1 ? arrive_add(a, (m.b + s) * a.Hkv + m.kvh, 1u) + 1u : 0u;
-#pragma unroll
-      for (int s = 0; s < kSpp; ++s)
-        if ((live >> s) & 1) complete(a, (m.b + s) * a.Hkv + m.kvh, pieces, after[s], s_w);
+      stage<C>(st, l, g, n16, s_k);
+      if (lane == 0) put_entry(s_ent, nent, m.b * a.Hkv + m.kvh, j == 0 ? np + pieces : 0, np + j, 0, 0, k);
+      return nent + 1;
     }
+    stage<16>(st, l, g, n16, s_k);
+#pragma unroll
+    for (int s = 0; s < kSpp; ++s) {
+      const int b = m.b + s;
+      const int Lb = load_uniform(a.context_lens + min(b, B - 1));  // in bounds either way
+      if (b < B && own_tiles(Lb, pg.Tp) > 0) {
+        if (lane == 0) put_entry(s_ent, nent, b * a.Hkv + m.kvh, 0, j, s, 1, k);
+        ++nent;
+      }
+    }
+    return nent;
   }
 
-  // `after` = the counter after this arrival; the one that completes it
-  // combines np + no partials and re-arms the counter.
-  static __device__ __forceinline__ void complete(const DecodeArgs& a, int seg, int np, uint32_t after,
-                                                  float* s_w) {
-    const uint32_t no = (after >> 16) & 0x7FFFu;
-    if ((after >> 31) && (after & 0xFFFFu) == uint32_t(np) + no)
-      K::finish(a, seg, np + int(no), s_w);
+  // Write out the parked partials (and the piece counts).
+  static __device__ __forceinline__ void flush(const DecodeArgs& a, int nent, const float* s_stage,
+                                               const int* s_ent) {
+    for (int e = 0; e < nent; ++e) {
+      const int seg = __builtin_amdgcn_readfirstlane(s_ent[3 * e]);
+      const int count = __builtin_amdgcn_readfirstlane(s_ent[3 * e + 1]);
+      const int w = __builtin_amdgcn_readfirstlane(s_ent[3 * e + 2]);
+      const int j = w & 0xFF, s = (w >> 8) & 0xFF, k = w >> 20;
+      const float* s_k = s_stage + k * kStage;
+      if ((w >> 16) & 0xF)
+        write_rows(a, seg, j, s_k + s * C * D, s_k + 16 * D + s * C, s_k + 16 * D + 16 + s * C);
+      else
+        write_rows(a, seg, j, s_k, s_k + C * D, s_k + C * D + C);
+      if (count > 0 && (threadIdx.x & (kWave - 1)) == 0) a.counters[seg] = uint32_t(count);
+    }
   }
 
   // The step's new row (token L - 1, an own tile) of every sequence whose
@@ -356,6 +367,20 @@ struct PrefixKernel {
   }
 };
 
+// The combine launch: output seg = (sequence, kv head) of block seg (a
+// grid-stride loop beyond the grid) combines the pieces its counter holds
+// and clears it; a counter of 0 (no own tiles: no output) is skipped.
+template <int D, int C, bool FP8>
+__global__ __launch_bounds__(kWave) void prefix_combine_kernel(DecodeArgs a, int nseg) {
+  using K = StreamKernel<D, C, FP8, kModeCombine, false, false>;
+  __shared__ float s_w[2 * C * kMaxStepPartitions];
+  for (int seg = blockIdx.x; seg < nseg; seg += gridDim.x) {
+    const int pieces = __builtin_amdgcn_readfirstlane(int(a.counters[seg]));
+    if (pieces > 0) K::finish(a, seg, pieces, s_w);
+  }
+}
+
+
 template <int D, int C, bool FP8, int MODE, bool EXT>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<FP8>(), 8)))
 void decode_prefix_kernel(DecodeArgs a, int B, int workers) {
@@ -370,8 +395,8 @@ void decode_prefix_kernel(DecodeArgs a, int B, int workers) {
   const int k_off = n16 * Geo::kRow + g * 16;
   const int v_off = (4 * g) * Geo::kRow + n16 * Geo::kVBytes;
 
-  __shared__ float s_w[2 * C * kMaxStepPartitions];  // combine weights
-  __shared__ float s_stage[P::kStage];                 // a piece's partial
+  __shared__ float s_stage[P::kSlots * P::kStage];  // parked partials
+  __shared__ int s_ent[3 * P::kEntries];            // their rows
 
   PrefixGeom pg;
   pg.Tp = a.prefix_tiles;
@@ -422,6 +447,8 @@ void decode_prefix_kernel(DecodeArgs a, int B, int workers) {
       if (k < NB - 1) P::issue(tl[k], a, mt[k], live, k_off, v_off);
     }
 
+    int npark = 0, nent = 0;  // parked pieces and their row entries
+
     auto step = [&](MTile<D, FP8>& x, const Meta& mx, const half8_t* qx, MTile<D, FP8>& y, Meta& my,
                     half8_t* qy, int64_t t) {
       const bool live = t + NB - 1 < t1;
@@ -447,7 +474,12 @@ void decode_prefix_kernel(DecodeArgs a, int B, int workers) {
         return;
       }
       if (mx.last) {
-        P::piece_end(a, B, mx, st, rg, pg, rw, t0, t1, g, n16, s_stage, s_w);
+        if (npark == P::kSlots) {
+          P::flush(a, nent, s_stage, s_ent);
+          npark = nent = 0;
+        }
+        nent = P::park(a, B, mx, st, rg, pg, rw, t0, t1, g, n16, npark, s_stage, s_ent, nent);
+        ++npark;
         K::reset(st);
       }
     };
@@ -460,7 +492,13 @@ void decode_prefix_kernel(DecodeArgs a, int B, int workers) {
         if (++t >= t1) break;
       }
     }
-    P::piece_end(a, B, mfin, st, rg, pg, rw, t0, t1, g, n16, s_stage, s_w);
+    // the range's last piece, and every piece parked before it
+    if (npark == P::kSlots) {
+      P::flush(a, nent, s_stage, s_ent);
+      npark = nent = 0;
+    }
+    nent = P::park(a, B, mfin, st, rg, pg, rw, t0, t1, g, n16, npark, s_stage, s_ent, nent);
+    P::flush(a, nent, s_stage, s_ent);
   }
 
   // sequences with no tokens: zero output rows, one wave each
@@ -479,6 +517,11 @@ hipError_t launch_prefix(const DecodeArgs& a, int B, hipStream_t stream) {
   else
     hipLaunchKernelGGL((decode_prefix_kernel<D, C, FP8, MODE, false>), dim3(workers), dim3(kWave), 0,
                        stream, a, B, workers);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nseg = B * a.Hkv;
+  hipLaunchKernelGGL((prefix_combine_kernel<D, C, FP8>), dim3(min(nseg, 2 * workers)), dim3(kWave), 0,
+                     stream, a, nseg);
   return hipGetLastError();
 }
 

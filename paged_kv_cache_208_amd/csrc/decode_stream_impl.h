@@ -692,6 +692,11 @@ template <int D, int C, bool FP8, int MODE, bool EXT, bool CACHED>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<FP8>(), 8)))
 void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   using K = StreamKernel<D, C, FP8, MODE, EXT, CACHED>;
+  // without QK-norm the pieces of split segments are combined by a second
+  // launch (stream_combine_kernel); with it, by the piece that arrives last
+  // (it also writes q' back, which no other wave may do before every piece
+  // of the segment has read q)
+  constexpr bool TWO = !K::QKNORM;
   const int win = K::W(a);
   using Geo = MfmaGeo<D, FP8>;
   static_assert(C <= 16, "head slots of one 16-wide product");
@@ -868,14 +873,14 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
           pseg = seg;
           ppieces = pieces;
           pj = int(rw - r_first);
-          K::write_partial(a, K::seg_row0(a, pseg), pj, s_pend);
+          if constexpr (!TWO) K::write_partial(a, K::seg_row0(a, pseg), pj, s_pend);
           pend = 1;
           K::reset(st);
           return;
         }
         K::reset(st);
       }
-      if (pend == 1) {
+      if (!TWO && pend == 1) {
         // the partial's stores were issued before this step's tile loads;
         // everything but the newest NB - 1 tiles' loads has completed
         issue_fence();
@@ -908,6 +913,12 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       K::stage_partial(st, l, g, n16, s_fin);
       K::write_partial(a, K::seg_row0(a, fseg), int(rw - f_first), s_fin);
     }
+    if constexpr (TWO) {
+      // the parked piece goes out now; a split segment's first piece tells
+      // the combine launch how many pieces to combine
+      if (pend == 1) K::write_partial(a, K::seg_row0(a, pseg), pj, s_pend);
+      if (fpieces > 1 && f_first == rw && lane == 0) a.counters[fseg] = uint32_t(fpieces);
+    } else {
     uint32_t fprev = 0;
     if (pend == 1 || fpieces > 1) {
       __builtin_amdgcn_s_waitcnt(0);  // partials at device scope
@@ -932,6 +943,7 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
       if (pfin) K::write_q_stashed(a, pseg, s_q, g, n16);
       if (ffin) K::write_q(a, fseg, qop, g, n16);
     }
+    }
   }
 
   // sequences with no tokens: zero output rows, one wave each
@@ -939,6 +951,19 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
     if (load_uniform(a.context_lens + b) == 0)
       for (int i = lane; i < K::NQ(a) * a.Hq * D; i += kWave)
         static_cast<_Float16*>(a.out)[size_t(b) * K::NQ(a) * a.Hq * D + i] = (_Float16)0.0f;
+}
+
+// The combine launch of the balanced step (modes without QK-norm): segment
+// seg (a grid-stride loop beyond the grid) combines the pieces its counter
+// holds and clears it; 0 = a segment that one wave finished.
+template <int D, int C, bool FP8, bool EXT>
+__global__ __launch_bounds__(kWave) void stream_combine_kernel(DecodeArgs a, int nseg) {
+  using K = StreamKernel<D, C, FP8, kModeCombine, EXT, false>;
+  __shared__ float s_w[2 * C * kMaxStepPartitions];
+  for (int seg = blockIdx.x; seg < nseg; seg += gridDim.x) {
+    const int pieces = __builtin_amdgcn_readfirstlane(int(a.counters[seg]));
+    if (pieces > 0) K::finish(a, seg, pieces, s_w);
+  }
 }
 
 // Compute units of the current device (queried once per device).
@@ -966,6 +991,16 @@ hipError_t launch_stream(const DecodeArgs& a, int B, hipStream_t stream) {
   else
     hipLaunchKernelGGL((decode_stream_kernel<D, C, FP8, MODE, false, CACHED>), dim3(workers),
                        dim3(kWave), 0, stream, a, B, workers);
+  if constexpr ((MODE & kModeQkNorm) != 0) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nseg = B * a.Hkv * (ext ? a.cgroups : 1);
+  if (ext)
+    hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, true>), dim3(min(nseg, 2 * workers)), dim3(kWave),
+                       0, stream, a, nseg);
+  else
+    hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, false>), dim3(min(nseg, 2 * workers)), dim3(kWave),
+                       0, stream, a, nseg);
   return hipGetLastError();
 }
 
