@@ -37,25 +37,33 @@ from paged_kv_cache_208_amd.roofline import HBM_GBPS  # noqa: E402
 METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + decode steps/s at B"
 ROTATE_BYTES = 1 << 30
 
-# HBM bytes per launch of the one-launch step kernel (balanced split), from two
-# rocprofv3 passes (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by
-# what the counter reads for a plain 256 MiB copy (x2.0 and x1.0).  Keyed by
-# workload and a hash of the step kernel's sources: a changed kernel reports
-# traffic null until it is measured again.
+# HBM bytes per step of the balanced step (its attend launch plus, without
+# QK-norm, its combine launch), from two rocprofv3 passes (FETCH_SIZE,
+# WRITE_SIZE in KiB per dispatch), each scaled by what the counter reads for a
+# plain 256 MiB copy (x2.0 and x1.0).  Keyed by workload and a hash of the step
+# kernels' sources: a changed kernel reports traffic null until it is measured
+# again.
 STEP_SOURCES = ("decode_stream.hip", "decode_stream_cached.hip", "decode_stream_impl.h",
                 "decode_stream_prefix.hip", "decode_prefix_impl.h", "decode_tile.h", "device.h",
                 "kernels.h", "shape_limits.h")
 # The key's last two fields are the shared-blocks hint and the shared prefix
 # (in blocks) that the run passed.
 MEASURED_TRAFFIC = {
-    ("c2", "32f3f6bf4166b822", False, 0): {"fetch_bytes": 316791232, "write_bytes": 3328384,
-                                        "source": "profiles/step_balanced_c2_hbm_bytes.md"},
-    ("c3", "32f3f6bf4166b822", True, 0): {"fetch_bytes": 579730144, "write_bytes": 6058629,
-                                       "source": "profiles/step_balanced_c3_c4_c5_hbm_bytes.md"},
-    ("c4", "32f3f6bf4166b822", False, 0): {"fetch_bytes": 4285991456, "write_bytes": 10026891,
-                                        "source": "profiles/step_balanced_c3_c4_c5_hbm_bytes.md"},
-    ("c5", "32f3f6bf4166b822", False, 0): {"fetch_bytes": 564210315, "write_bytes": 12873760,
-                                        "source": "profiles/step_balanced_c3_c4_c5_hbm_bytes.md"},
+    ("c2", "8b828d405733b42b", False, 0): {"fetch_bytes": 316715488, "write_bytes": 3340288,
+        "attend_fetch_bytes": 313846219, "combine_fetch_bytes": 2869269,
+        "source": "profiles/step_hbm_bytes.md"},
+    ("c3", "8b828d405733b42b", False, 64): {"fetch_bytes": 569343552, "write_bytes": 9895936,
+        "attend_fetch_bytes": 561327637, "combine_fetch_bytes": 8015915,
+        "source": "profiles/step_hbm_bytes.md"},
+    ("c3", "8b828d405733b42b", True, 0): {"fetch_bytes": 570291637, "write_bytes": 6018240,
+        "attend_fetch_bytes": 565791829, "combine_fetch_bytes": 4499808,
+        "source": "profiles/step_hbm_bytes.md"},
+    ("c4", "8b828d405733b42b", False, 0): {"fetch_bytes": 4285237099, "write_bytes": 10022155,
+        "attend_fetch_bytes": 4285237099, "combine_fetch_bytes": 0,
+        "source": "profiles/step_hbm_bytes.md"},
+    ("c5", "8b828d405733b42b", False, 0): {"fetch_bytes": 563718624, "write_bytes": 12840965,
+        "attend_fetch_bytes": 552547680, "combine_fetch_bytes": 11170944,
+        "source": "profiles/step_hbm_bytes.md"},
 }
 
 def step_source_hash():
@@ -685,6 +693,15 @@ def main():
     kernel_ms = min(ms, dec_avg) if one_launch else dec_b2b
     achieved = kv_unique / (kernel_ms * 1e-3) / 1e9
     unique_rate = kv_unique / (ms * 1e-3) / 1e9
+    # launches per step: the unfused path's append, decode and reduce; the
+    # one-launch fixed partitions; the balanced split's attend and combine
+    # (one launch with QK-norm inside the step); a chunk's append before it
+    if args.unfused:
+        launches = (3 if not fp8 else 2) if PS else (2 if not fp8 else 1)
+    elif step_ps:
+        launches = 1
+    else:
+        launches = (1 if cfg.fused_append and not chunk else 2) + (1 if chunk and not fp8 else 0)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -709,8 +726,7 @@ def main():
             "step": ("attend+combine" if fp8 else
                      ("qknorm_rope+append+attend+combine" if cfg.fused_append
                       else "append+attend+combine")),
-            "launches_per_step": ((3 if not fp8 else 2) if args.unfused and PS
-                                  else 2 if (chunk and not fp8) or prefix_blocks else 1),
+            "launches_per_step": launches,
             "window": args.window,
             "new_tokens_per_sequence": nq,
             "shared_prefix_blocks": prefix_blocks,
