@@ -246,13 +246,16 @@ int paged_attn_reduce(void* out, const float* part_out, const float* part_max,
  *   max_partitions >= 6 (a sequence's prefix and own parts take up to
  *   max_partitions / 2 pieces each); prefix_blocks < 0 or > MBS is
  *   PKV_EINVAL.  0 = no shared prefix.
- * kv_dtype PKV_KV_E4M3: attend + combine only (k_new must be NULL); either
- *   dtype may carry PKV_KV_SHARED_BLOCKS.
+ * kv_dtype PKV_KV_E4M3: k_new != NULL (n_query == 1, no QK-norm, else
+ *   PKV_EUNSUPPORTED) appends each sequence's new row at position L_b - 1
+ *   with paged_kv_append_e4m3's policy, updating k_scale / v_scale (one more
+ *   launch, ahead of the attention); k_new == NULL attends to the pools as
+ *   they are.  Either dtype may carry PKV_KV_SHARED_BLOCKS.
  * L_b == 0: zero output row, nothing written to the pools, q untouched.
  * Errors and shape limits as for paged_attn_decode and paged_kv_append.
  */
 int paged_decode_step(void* out, void* q, const void* k_new, const void* v_new, void* k_pool,
-                      void* v_pool, const float* k_scale, const float* v_scale,
+                      void* v_pool, float* k_scale, float* v_scale,
                       const int32_t* block_tables, const int32_t* context_lens, int B, int Hq,
                       int Hkv, int D, int BS, int MBS, int64_t NB, float scale, int kv_dtype,
                       int partition_size, int window, int n_query, int prefix_blocks,
@@ -340,8 +343,8 @@ int paged_kv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_sc
  * paged_decode_step_static_partitions(...).
  */
 int paged_decode_step_static(void* out, void* q, const void* k_new, const void* v_new,
-                             void* k_pool, void* v_pool, const float* k_scale,
-                             const float* v_scale, const int32_t* block_tables,
+                             void* k_pool, void* v_pool, float* k_scale,
+                             float* v_scale, const int32_t* block_tables,
                              const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
                              int MBS, int64_t NB, float scale, int kv_dtype, int partition_size,
                              int window, int n_query, int prefix_blocks, const float* gamma_q,

@@ -351,7 +351,9 @@ def paged_decode_step(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                       v_new=None, k_scale=None, v_scale=None, partition_size=0, window=0,
                       prefix_blocks=0, gamma_q=None, gamma_k=None, eps=1e-6, rope_theta=1e6,
                       workspace=None, shared_blocks=False, stream=None):
-    """Append (optional, + Qwen3 QK-norm/RoPE) + decode + combine in one launch.
+    """Append (optional: fp16 rows, + Qwen3 QK-norm/RoPE, or E4M3 rows through
+    the E4M3 append policy) + decode + combine, enqueued as one to three
+    launches.
     ``workspace`` is alloc_step_workspace(...)'s tuple.  partition_size 0
     splits contexts evenly over all waves into at most workspace-depth
     pieces; > 0 uses fixed partitions.  window > 0 attends to the last

@@ -138,8 +138,8 @@ extern "C" int paged_attn_reduce(void* out, const float* part_out, const float* 
 }
 
 extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const void* v_new,
-                                 void* k_pool, void* v_pool, const float* k_scale,
-                                 const float* v_scale, const int32_t* block_tables,
+                                 void* k_pool, void* v_pool, float* k_scale,
+                                 float* v_scale, const int32_t* block_tables,
                                  const int32_t* context_lens, int B, int Hq, int Hkv, int D,
                                  int BS, int MBS, int64_t NB, float scale, int kv_dtype,
                                  int partition_size, int window, int n_query,
@@ -189,7 +189,18 @@ extern "C" int paged_decode_step(void* out, void* q, const void* k_new, const vo
   a.theta = rope_theta;
   a.counters = counters;
   int mode = pkv::kModeCombine;
-  if (k_new) mode |= pkv::kModeAppend;
+  if (k_new && fp8) {
+    // E4M3: the new rows (and their blocks' scales) are written by the E4M3
+    // append first; the attention then reads them from the pools
+    pkv::AppendE4m3Args ap{k_new, v_new, static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                           k_scale, v_scale, nullptr, Hkv, BS,
+                           block_tables, context_lens, MBS};
+    const int sa = launch_status(pkv::launch_append_e4m3(ap, B, D, static_cast<hipStream_t>(stream)));
+    if (sa != PKV_OK) return sa;
+    a.k_new = a.v_new = nullptr;
+  } else if (k_new) {
+    mode |= pkv::kModeAppend;
+  }
   if (gamma_k) mode |= pkv::kModeQkNorm;
   if (prefix_blocks > 0)  // balanced split, shared prefix read once per group of sequences
     return launch_status(pkv::launch_decode_prefix(a, B, D, a.ncols, fp8, mode,
@@ -277,8 +288,8 @@ extern "C" int paged_decode_step_static_partitions(int B, int Hq, int Hkv, int D
 }
 
 extern "C" int paged_decode_step_static(void* out, void* q, const void* k_new, const void* v_new,
-                                        void* k_pool, void* v_pool, const float* k_scale,
-                                        const float* v_scale, const int32_t* block_tables,
+                                        void* k_pool, void* v_pool, float* k_scale,
+                                        float* v_scale, const int32_t* block_tables,
                                         const int32_t* context_lens, int B, int Hq, int Hkv, int D,
                                         int BS, int MBS, int64_t NB, float scale, int kv_dtype,
                                         int partition_size, int window, int n_query,

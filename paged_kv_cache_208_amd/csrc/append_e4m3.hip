@@ -13,7 +13,8 @@
 //
 // One wave per (token, kv head, pool): the new row is D fp16 values (one or
 // two per lane), the block's earlier rows r * D bytes (four per lane per
-// pass); blocks of 16 or 32 tokens.
+// pass); blocks of 16 or 32 tokens.  The decode step appends through this
+// kernel too, each sequence's new token at its last position.
 #include "device.h"
 #include "kernels.h"
 
@@ -35,7 +36,13 @@ __global__ __launch_bounds__(kWave) void append_e4m3_kernel(AppendE4m3Args a) {
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
   const int lane = threadIdx.x;
-  const int64_t slot = a.slot_mapping[t];
+  int64_t slot = -1;
+  if (a.slot_mapping) {
+    slot = a.slot_mapping[t];
+  } else {
+    const int L = a.context_lens[t];
+    if (L > 0) slot = int64_t(a.block_tables[size_t(t) * a.MBS + (L - 1) / a.bs]) * a.bs + (L - 1) % a.bs;
+  }
   if (slot < 0) return;
   const int64_t n = slot / a.bs;
   const int r = int(slot % a.bs);

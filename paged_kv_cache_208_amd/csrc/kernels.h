@@ -79,9 +79,14 @@ struct AppendE4m3Args {
   uint8_t* v_pool;
   float* k_scale;             // [NB][Hkv]
   float* v_scale;
-  const int64_t* slot_mapping;  // [T]
+  const int64_t* slot_mapping;  // [T]; NULL: token t is sequence t's last one (below)
   int Hkv;
   int bs;                     // tokens per block (16 or 32)
+  // without slot_mapping: token t goes to position context_lens[t] - 1 of
+  // sequence t (block_tables [T][MBS]); sequences with no tokens are skipped
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int MBS;
 };
 
 struct CopyArgs {

@@ -198,7 +198,12 @@ extern "C" int pkv_validate_step(const void* out, const void* q, const void* k_n
       return PKV_EUNSUPPORTED;
   }
   if (k_new != nullptr) {
-    if ((kv_dtype & ~PKV_KV_SHARED_BLOCKS) != PKV_KV_F16) return PKV_EUNSUPPORTED;
+    // E4M3 rows go through the E4M3 append (its own launch ahead of the
+    // attention), one new token per sequence: its slots lie in distinct
+    // blocks, as that append requires; no QK-norm
+    if ((kv_dtype & ~PKV_KV_SHARED_BLOCKS) == PKV_KV_E4M3 && (n_query != 1 || gamma_k != nullptr))
+      return PKV_EUNSUPPORTED;
+    if (int64_t(B) > pkv::kMaxGrid || Hkv > 65535) return PKV_EUNSUPPORTED;
     if (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return PKV_EINVAL;
   } else if (v_new != nullptr) {
     return PKV_EINVAL;

@@ -226,10 +226,12 @@ def _step_args(**kw):
     (dict(gamma_q=A), -1),
     (dict(gamma_k=A, gamma_q=A, k_new=None, v_new=None), -1),
     (dict(gamma_k=A, gamma_q=A, theta=-1.0), -1),
-    (dict(kv_dtype=1, k_scale=A, v_scale=A), -2),
+    (dict(kv_dtype=1, k_scale=A, v_scale=A), 0),          # E4M3 append, one new token
     (dict(kv_dtype=1, k_scale=A, v_scale=A, k_new=None, v_new=None), 0),
+    (dict(kv_dtype=1, k_scale=A, v_scale=A, partition_size=0, max_partitions=16, n_query=2), -2),
+    (dict(kv_dtype=1, k_scale=A, v_scale=A, gamma_k=A, gamma_q=A), -2),  # no E4M3 QK-norm
     (dict(kv_dtype=0x100), 0),                           # shared-blocks hint with the append
-    (dict(kv_dtype=0x101, k_scale=A, v_scale=A), -2),    # E4M3 does not append
+    (dict(kv_dtype=0x101, k_scale=A, v_scale=A), 0),
     (dict(kv_dtype=0x101, k_scale=A, v_scale=A, k_new=None, v_new=None), 0),
     (dict(kv_dtype=0x300), -1),
     (dict(D=96), -2),
