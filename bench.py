@@ -118,6 +118,9 @@ def parse():
     p.add_argument("--partition-size", type=int, default=None)
     p.add_argument("--rotate", type=int, default=None, help="copies of the inputs (default: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fp8-append", action="store_true",
+                   help="E4M3 workloads: the step also appends each sequence's new row\n"
+                        "(E4M3 append policy, one more launch)")
     p.add_argument("--tile-ceiling", type=int, default=1, choices=(0, 1),
                    help="1: also time pkv_tile_read over the step's own tiles (its practical\n"
                         "read ceiling for this access pattern)")
@@ -523,7 +526,7 @@ def main():
 
     def step_fused(g, i, timed):
         kw = {}
-        if not fp8:
+        if not fp8 or args.fp8_append:
             kw = dict(k_new=g["k_new"], v_new=g["v_new"])
             if cfg.fused_append:
                 kw.update(gamma_q=g["gamma_q"], gamma_k=g["gamma_k"], eps=cfg.eps,
@@ -678,7 +681,7 @@ def main():
     tokens = int(d["context_lens"].astype(np.int64).sum())
     traffic = None
     fused_balanced = (not args.unfused and step_ps == 0 and args.splits == 16 and not args.window
-                      and nq == 1)
+                      and nq == 1 and not args.fp8_append)
     measured = (MEASURED_TRAFFIC.get((cfg.name, step_source_hash(), shared, prefix_blocks))
                 if fused_balanced else None)
     if measured:
@@ -701,7 +704,8 @@ def main():
     elif step_ps:
         launches = 1
     else:
-        launches = (1 if cfg.fused_append and not chunk else 2) + (1 if chunk and not fp8 else 0)
+        launches = ((1 if cfg.fused_append and not chunk else 2) + (1 if chunk and not fp8 else 0)
+                    + (1 if fp8 and args.fp8_append else 0))
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -723,7 +727,7 @@ def main():
             "split": (f"fixed {PS}-token partitions" if args.unfused or step_ps
                       else f"balanced over all waves, <= {args.splits} pieces per sequence"),
             "context_tokens": tokens, "mean_context": round(tokens / cfg.B, 1),
-            "step": ("attend+combine" if fp8 else
+            "step": (("append+attend+combine" if args.fp8_append else "attend+combine") if fp8 else
                      ("qknorm_rope+append+attend+combine" if cfg.fused_append
                       else "append+attend+combine")),
             "launches_per_step": launches,
