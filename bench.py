@@ -424,6 +424,12 @@ def main():
         bench_append_e4m3(args, cfg, d)
         return
 
+    if args.fp8_append and cfg.kv_dtype == "e4m3" and d.get("k_new") is None:
+        # the new rows the E4M3 step appends (fp16 N(0, 1), a seeded draw of
+        # their own)
+        rng = np.random.default_rng(208_900)
+        d = dict(d, k_new=rng.standard_normal((cfg.B, cfg.Hkv, cfg.D)).astype(np.float16),
+                 v_new=rng.standard_normal((cfg.B, cfg.Hkv, cfg.D)).astype(np.float16))
     nq = args.n_query
     # a chunk wider than one 16-column product (g * nq > 16) is appended by
     # paged_kv_append (one slot per new token, QK-norm + RoPE at each token's
