@@ -80,7 +80,8 @@ def step_tile_ids(cfg, d, nq, prefix_blocks, cached):
     head, then sequence, then column group, then tile; with a shared prefix,
     per kv head the prefix once per group of 16 / g sequences, then each
     sequence's own tiles), as int32 tile indices for pkv_tile_read (~index:
-    read with the default cache policy)."""
+    read with the default cache policy, as the step does for every tile
+    under the shared-blocks hint)."""
     tab, lens = d["block_tables"], d["context_lens"].astype(np.int64)
     g = cfg.Hq // cfg.Hkv
     hb = cfg.block_size // 16                      # tiles per block
@@ -97,10 +98,12 @@ def step_tile_ids(cfg, d, nq, prefix_blocks, cached):
             tp = prefix_blocks * hb
             spp = 16 // g
             for lead in range(0, cfg.B, spp):
-                out.append(~seq_tiles(lead, kvh, 0, tp))
+                t = seq_tiles(lead, kvh, 0, tp)
+                out.append(~t if cached else t)
             for b in range(cfg.B):
                 if ntile[b] > tp:
-                    out.append(seq_tiles(b, kvh, tp, ntile[b]))
+                    t = seq_tiles(b, kvh, tp, ntile[b])
+                    out.append(~t if cached else t)
         else:
             for b in range(cfg.B):
                 t = seq_tiles(b, kvh, 0, ntile[b])
@@ -741,8 +744,7 @@ def main():
             "new_tokens_per_sequence": nq,
             "shared_prefix_blocks": prefix_blocks,
             "rotated_copies": R,
-            "kv_load_policy": ("prefix tiles cached, own tiles non-temporal" if prefix_blocks
-                               else "cached (shared-blocks hint)" if shared else "non-temporal"),
+            "kv_load_policy": "cached (shared-blocks hint)" if shared else "non-temporal",
         },
         "steps_per_s": round(1e3 / ms, 1),
         "tokens_per_s": round(cfg.B * nq * 1e3 / ms, 1),

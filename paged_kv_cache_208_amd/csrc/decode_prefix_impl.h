@@ -13,11 +13,7 @@
 // (a prefix span is the Tp prefix tiles with the group's 16 columns; a
 // sequence's own tiles are the ones after the prefix, with its g columns).
 // The waves' ranges split this order evenly exactly as in the plain
-// balanced step.  Every (sequence, kv head) output combines its group's
-// prefix pieces and its own pieces (log-sum-exp, as paged_attn_reduce
-// does); prefix tiles are loaded with the default cache policy (the other
-// groups of the kv head read them next, on the same XCD), own tiles with
-// the non-temporal one.
+// balanced step.  All tiles load with the non-temporal policy.
 //
 // Every (sequence, kv head) output combines its group's np prefix pieces
 // and its own pieces (log-sum-exp, as paged_attn_reduce does), in a second
@@ -206,14 +202,14 @@ struct PrefixKernel {
       qop[c] = __builtin_bit_cast(half8_t, buffer_load16(r, (row * D + qk_dim0<FP8>(c, g)) * int(sizeof(_Float16))));
   }
 
-  // Prefix tiles with the default cache policy (the group's neighbours
-  // read them next), own tiles streamed.
+  // Every tile is streamed (non-temporal): with the prefix read once per
+  // group instead of once per sequence, keeping it cached gains less than a
+  // load form chosen per tile costs in the loop.
   static __device__ __forceinline__ void issue(MTile<D, FP8>& t, const DecodeArgs& a, const Meta& m,
                                                bool live, int k_off, int v_off) {
     const size_t base =
         live ? ((size_t(m.id) * a.Hkv + m.kvh) * K::BST(a) + m.half) * Geo::kTile : 0;
-    load_mtile_at<D, FP8>(t, a, base, live ? min(16, m.L - 16 * (m.f + m.n)) : 0, k_off, v_off,
-                          live && m.kind == 1);
+    load_mtile_at<D, FP8>(t, a, base, live ? min(16, m.L - 16 * (m.f + m.n)) : 0, k_off, v_off);
     t.lo = 0;
   }
 

@@ -39,13 +39,18 @@ def test_prefix_order_reads_the_prefix_once_per_group():
     g = cfg.Hq // cfg.Hkv
     groups = -(-cfg.B // (16 // g))
     own = np.maximum(-(-d["context_lens"].astype(np.int64) // 16) - tp, 0).sum()
-    assert (ids < 0).sum() == cfg.Hkv * groups * tp
-    assert (ids >= 0).sum() == cfg.Hkv * own
-    # every prefix tile read is one of the Hkv * tp shared tiles
+    assert len(ids) == cfg.Hkv * (groups * tp + own) and (ids >= 0).all()
     shared = {int(blk) * cfg.Hkv + h for blk in d["block_tables"][0, :tp] for h in range(cfg.Hkv)}
-    assert set((~ids[ids < 0]).tolist()) == shared
-    # no own tile is a shared one
-    assert not (set(ids[ids >= 0].tolist()) & shared)
+    per_head = groups * tp + own
+    for h in range(cfg.Hkv):
+        head = ids[h * per_head:(h + 1) * per_head]
+        # the head's prefix spans first: its tp shared tiles, once per group,
+        # then its own tiles, none of them shared
+        assert set(head[:groups * tp].tolist()) == {t for t in shared if t % cfg.Hkv == h}
+        assert np.array_equal(head[:groups * tp], np.tile(head[:tp], groups))
+        assert not (set(head[groups * tp:].tolist()) & shared)
+    # with the cache hint every index is flipped
+    assert np.array_equal(~bench.step_tile_ids(cfg, d, 1, tp, True), ids)
 
 
 def test_column_groups_repeat_each_sequence():
