@@ -49,20 +49,20 @@ STEP_SOURCES = ("decode_stream.hip", "decode_stream_cached.hip", "decode_stream_
 # The key's last two fields are the shared-blocks hint and the shared prefix
 # (in blocks) that the run passed.
 MEASURED_TRAFFIC = {
-    ("c2", "8b828d405733b42b", False, 0): {"fetch_bytes": 316715488, "write_bytes": 3340288,
-        "attend_fetch_bytes": 313846219, "combine_fetch_bytes": 2869269,
+    ("c2", "8f61117f6d51c687", False, 0): {"fetch_bytes": 316679157, "write_bytes": 3340288,
+        "attend_fetch_bytes": 313809899, "combine_fetch_bytes": 2869259,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c3", "8b828d405733b42b", False, 64): {"fetch_bytes": 569343552, "write_bytes": 9895936,
-        "attend_fetch_bytes": 561327637, "combine_fetch_bytes": 8015915,
+    ("c3", "8f61117f6d51c687", False, 64): {"fetch_bytes": 589974208, "write_bytes": 9895936,
+        "attend_fetch_bytes": 581957536, "combine_fetch_bytes": 8016672,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c3", "8b828d405733b42b", True, 0): {"fetch_bytes": 570291637, "write_bytes": 6018240,
-        "attend_fetch_bytes": 565791829, "combine_fetch_bytes": 4499808,
+    ("c3", "8f61117f6d51c687", True, 0): {"fetch_bytes": 570358880, "write_bytes": 6018267,
+        "attend_fetch_bytes": 565859339, "combine_fetch_bytes": 4499541,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c4", "8b828d405733b42b", False, 0): {"fetch_bytes": 4285237099, "write_bytes": 10022155,
-        "attend_fetch_bytes": 4285237099, "combine_fetch_bytes": 0,
+    ("c4", "8f61117f6d51c687", False, 0): {"fetch_bytes": 4285758955, "write_bytes": 10022144,
+        "attend_fetch_bytes": 4285758955, "combine_fetch_bytes": 0,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c5", "8b828d405733b42b", False, 0): {"fetch_bytes": 563718624, "write_bytes": 12840965,
-        "attend_fetch_bytes": 552547680, "combine_fetch_bytes": 11170944,
+    ("c5", "8f61117f6d51c687", False, 0): {"fetch_bytes": 563737515, "write_bytes": 12840965,
+        "attend_fetch_bytes": 552566624, "combine_fetch_bytes": 11170891,
         "source": "profiles/step_hbm_bytes.md"},
 }
 
