@@ -14,7 +14,7 @@ namespace {
 int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
 
 // ---------------------------------------------------------------------------
-// Static scratch of paged_decode_step_static: the arrival counters (first
+// Static scratch of paged_decode_step_static: the step's counters (first
 // kScratchCounterBytes, zero between calls) and then the partials.  One copy
 // per GPU, held until the process ends.  The host never uses the array's
 // name as an address (in host code it is only a stand-in for the symbol):

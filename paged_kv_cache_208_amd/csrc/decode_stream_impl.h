@@ -1,6 +1,7 @@
 // Balanced decode step for gfx950: append (+ QK-norm/RoPE), attention and
-// the combine of split contexts in one launch, with every wave given the
-// same amount of KV to read.
+// the combine of split contexts, with every wave given the same amount of
+// KV to read: an attend launch and a combine launch, or one launch with
+// QK-norm.
 //
 // The batch's tiles are laid out in one flattened order: kv head, then
 // sequence b, then the sequence's 16-token tiles ("Distributed LLM Inference
@@ -19,10 +20,12 @@
 //
 // A segment that lies inside one wave's range is finished by that wave (the
 // normalised output is written directly).  A segment shared by several
-// consecutive waves leaves one partial (m, l, o) per wave; the last wave to
-// finish its piece combines them (log-sum-exp), as paged_attn_reduce does.
-// Partials and arrival counters use device-scope coherent accesses; the
-// counters return to zero.
+// consecutive waves leaves one partial (m, l, o) per wave, combined
+// (log-sum-exp, as paged_attn_reduce does) by the combine launch, which
+// reads the piece count the segment's first piece left in its counter.
+// With QK-norm the last wave to finish its piece combines them in the same
+// launch (and writes q' back), counting arrivals with device-scope coherent
+// accesses.  The counters return to zero either way.
 //
 // Inside the loop a wave issues only loads (KV tiles, and q when a tile
 // starts a segment): vector memory operations complete in issue order, so a
@@ -571,8 +574,9 @@ struct StreamKernel {
   }
 
   // Log-sum-exp combine of the `pieces` partials of segment seg's C columns
-  // (one wave; weights staged in LDS), done by the last piece to arrive,
-  // which then re-arms the counter.  A lane owns float4 pieces of the C rows.
+  // (one wave; weights staged in LDS), done by the combine launch or by the
+  // last piece to arrive, which then clears the counter.  A lane owns float4
+  // pieces of the C rows.
   // The loads of the statistics and of the first batch of partial rows all
   // go out together (one round trip when pieces <= kBatch); a wave that
   // finishes two segments issues both segments' loads before computing
@@ -809,15 +813,16 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
     }
 
     // A shared segment whose piece ends before the range does (only the
-    // range's first segment can: it is that segment's last piece) publishes
-    // its partial right away and arrives one loop step later, so that the
-    // segment's combine falls to one of the waves whose ranges end with its
-    // other pieces, and no wave has two combines to do when its range ends.
-    // The partial's stores go out behind the next tile's loads; one step
-    // later a counted wait that leaves the newest tile's loads in flight
-    // (vector memory operations complete in issue order) makes sure they
-    // have completed before the arrival, whose result is read when the
-    // range is done.
+    // range's first segment can: it is that segment's last piece) is parked
+    // in LDS.  Without QK-norm it is written out when the range ends.  With
+    // QK-norm it publishes its partial right away and arrives one loop step
+    // later, so that the segment's combine falls to one of the waves whose
+    // ranges end with its other pieces, and no wave has two combines to do
+    // when its range ends: the partial's stores go out behind the next
+    // tile's loads; one step later a counted wait that leaves the newest
+    // tile's loads in flight (vector memory operations complete in issue
+    // order) makes sure they have completed before the arrival, whose
+    // result is read when the range is done.
     int pend = 0;  // 0 none, 1 partial written, 2 arrived (prev count in pprev)
     int pseg = 0, ppieces = 0, pj = 0;
     uint32_t pprev = 0;

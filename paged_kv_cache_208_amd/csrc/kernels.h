@@ -28,7 +28,7 @@ struct DecodeArgs {
   const float* gamma_q;       // [D] (QK-norm)
   const float* gamma_k;
   float eps, theta;
-  uint32_t* counters;         // [B][Hkv] arrivals per (sequence, kv head); zero between launches
+  uint32_t* counters;         // [B][Hkv * CG] piece counts or arrivals per segment; zero between steps
   int window;                 // > 0: attend to the last `window` tokens only (balanced step)
   int nq;                     // new query tokens per sequence (balanced step; 1 otherwise)
   int ncols;                  // query columns per (sequence, kv head): group * nq
