@@ -44,24 +44,26 @@ ROTATE_BYTES = 1 << 30
 # kernels' code (their sources without comments): a changed kernel reports
 # traffic null until it is measured again.
 STEP_SOURCES = ("decode_stream.hip", "decode_stream_cached.hip", "decode_stream_impl.h",
-                "decode_stream_prefix.hip", "decode_prefix_impl.h", "decode_tile.h", "device.h",
-                "kernels.h", "shape_limits.h")
+                "decode_tile.h", "device.h", "kernels.h", "shape_limits.h")
+# the shared-prefix step's own sources (its key hashes both sets)
+PREFIX_SOURCES = ("decode_stream_prefix.hip", "decode_prefix_impl.h")
 # The key's last two fields are the shared-blocks hint and the shared prefix
-# (in blocks) that the run passed.
+# (in blocks) that the run passed; its hash covers the plain step's sources,
+# and the prefix step's too for a shared-prefix run.
 MEASURED_TRAFFIC = {
-    ("c2", "f2bd61907f7ed363", False, 0): {"fetch_bytes": 316679157, "write_bytes": 3340288,
+    ("c2", "e2713ccdc7488767", False, 0): {"fetch_bytes": 316679157, "write_bytes": 3340288,
         "attend_fetch_bytes": 313809899, "combine_fetch_bytes": 2869259,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c3", "f2bd61907f7ed363", False, 64): {"fetch_bytes": 589974208, "write_bytes": 9895936,
-        "attend_fetch_bytes": 581957536, "combine_fetch_bytes": 8016672,
+    ("c3", "f8bc02b223875d8f", False, 64): {"fetch_bytes": 590526155, "write_bytes": 9895936,
+        "attend_fetch_bytes": 582510219, "combine_fetch_bytes": 8015936,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c3", "f2bd61907f7ed363", True, 0): {"fetch_bytes": 570358880, "write_bytes": 6018267,
+    ("c3", "e2713ccdc7488767", True, 0): {"fetch_bytes": 570358880, "write_bytes": 6018267,
         "attend_fetch_bytes": 565859339, "combine_fetch_bytes": 4499541,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c4", "f2bd61907f7ed363", False, 0): {"fetch_bytes": 4285758955, "write_bytes": 10022144,
+    ("c4", "e2713ccdc7488767", False, 0): {"fetch_bytes": 4285758955, "write_bytes": 10022144,
         "attend_fetch_bytes": 4285758955, "combine_fetch_bytes": 0,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c5", "f2bd61907f7ed363", False, 0): {"fetch_bytes": 563737515, "write_bytes": 12840965,
+    ("c5", "e2713ccdc7488767", False, 0): {"fetch_bytes": 563737515, "write_bytes": 12840965,
         "attend_fetch_bytes": 552566624, "combine_fetch_bytes": 11170891,
         "source": "profiles/step_hbm_bytes.md"},
 }
@@ -77,10 +79,10 @@ def code_of(text):
     return "\n".join(lines)
 
 
-def step_source_hash(read=None):
+def step_source_hash(read=None, prefix=False):
     import hashlib
     h = hashlib.sha256()
-    for name in STEP_SOURCES:
+    for name in STEP_SOURCES + (PREFIX_SOURCES if prefix else ()):
         path = os.path.join("paged_kv_cache_208_amd", "csrc", name)
         if read is None:
             with open(os.path.join(ROOT, path)) as f:
@@ -707,7 +709,8 @@ def main():
     traffic = None
     fused_balanced = (not args.unfused and step_ps == 0 and args.splits == 16 and not args.window
                       and nq == 1 and not args.fp8_append)
-    measured = (MEASURED_TRAFFIC.get((cfg.name, step_source_hash(), shared, prefix_blocks))
+    measured = (MEASURED_TRAFFIC.get((cfg.name, step_source_hash(prefix=prefix_blocks > 0), shared,
+                                      prefix_blocks))
                 if fused_balanced else None)
     if measured:
         traffic = measured["fetch_bytes"] + measured["write_bytes"]

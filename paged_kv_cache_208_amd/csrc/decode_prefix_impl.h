@@ -363,20 +363,6 @@ struct PrefixKernel {
   }
 };
 
-// The combine launch: output seg = (sequence, kv head) of block seg (a
-// grid-stride loop beyond the grid) combines the pieces its counter holds
-// and clears it; a counter of 0 (no own tiles: no output) is skipped.
-template <int D, int C, bool FP8>
-__global__ __launch_bounds__(kWave) void prefix_combine_kernel(DecodeArgs a, int nseg) {
-  using K = StreamKernel<D, C, FP8, kModeCombine, false, false>;
-  __shared__ float s_w[2 * C * kMaxStepPartitions];
-  for (int seg = blockIdx.x; seg < nseg; seg += gridDim.x) {
-    const int pieces = __builtin_amdgcn_readfirstlane(int(a.counters[seg]));
-    if (pieces > 0) K::finish(a, seg, pieces, s_w);
-  }
-}
-
-
 template <int D, int C, bool FP8, int MODE, bool EXT>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<FP8>(), 8)))
 void decode_prefix_kernel(DecodeArgs a, int B, int workers) {
@@ -516,8 +502,10 @@ hipError_t launch_prefix(const DecodeArgs& a, int B, hipStream_t stream) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nseg = B * a.Hkv;
-  hipLaunchKernelGGL((prefix_combine_kernel<D, C, FP8>), dim3(min(nseg, 2 * workers)), dim3(kWave), 0,
-                     stream, a, nseg);
+  // the balanced step's combine launch: one output (sequence, kv head) per
+  // segment, nq = 1, so the plain layout applies
+  hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, false>), dim3(min(nseg, 2 * workers)), dim3(kWave),
+                     0, stream, a, nseg);
   return hipGetLastError();
 }
 
