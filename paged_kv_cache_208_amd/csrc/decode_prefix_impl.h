@@ -230,7 +230,7 @@ struct PrefixKernel {
   }
 
   // Slot j of the C partial rows of segment seg from LDS: o rows at o, maxima
-  // at mv, sums at lv.
+  // at mv, sums at lv (plain stores: the combine launch reads them).
   static __device__ __forceinline__ void write_rows(const DecodeArgs& a, int seg, int j, const float* o,
                                                     const float* mv, const float* lv) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -240,12 +240,12 @@ struct PrefixKernel {
     for (int k = 0; k < K::kOwn; ++k) {
       const int c = lane + k * kWave;
       if (c < K::kF4)
-        store16_coherent(rs, K::partial_offset(a, c, j), *reinterpret_cast<const u32x4*>(o + 4 * c));
+        store16<false>(rs, K::partial_offset(a, c, j), *reinterpret_cast<const u32x4*>(o + 4 * c));
     }
     if (lane < C) {
       const size_t pr = (row0 + lane) * a.max_partitions + j;
-      store_f32<true>(a.part_max + pr, mv[lane]);
-      store_f32<true>(a.part_sum + pr, lv[lane]);
+      store_f32<false>(a.part_max + pr, mv[lane]);
+      store_f32<false>(a.part_sum + pr, lv[lane]);
     }
   }
 
@@ -504,7 +504,8 @@ hipError_t launch_prefix(const DecodeArgs& a, int B, hipStream_t stream) {
   const int nseg = B * a.Hkv;
   // the balanced step's combine launch: one output (sequence, kv head) per
   // segment, nq = 1, so the plain layout applies
-  hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, false>), dim3(min(nseg, 2 * workers)), dim3(kWave),
+  hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, false>), dim3(min(nseg, 2 * workers)),
+                     (combine_block<D, C, FP8, false>()),
                      0, stream, a, nseg);
   return hipGetLastError();
 }

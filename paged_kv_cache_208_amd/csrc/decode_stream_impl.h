@@ -555,7 +555,9 @@ struct StreamKernel {
   }
 
   // Piece j of the segment at output row row0, from its LDS copy: each lane
-  // writes whole 16-byte pieces of the rows, with device-scope coherence.
+  // writes whole 16-byte pieces of the rows.  With QK-norm a wave of the
+  // same launch combines them, so the stores are device-scope coherent; the
+  // combine launch reads them after the launch boundary, so plain stores do.
   static __device__ __forceinline__ void write_partial(const DecodeArgs& a, size_t row0, int j,
                                                        const float* s_o) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -564,19 +566,19 @@ struct StreamKernel {
     for (int k = 0; k < kOwn; ++k) {
       const int c = lane + k * kWave;
       if (c < kF4)
-        store16_coherent(rs, partial_offset(a, c, j), *reinterpret_cast<const u32x4*>(s_o + 4 * c));
+        store16<QKNORM>(rs, partial_offset(a, c, j), *reinterpret_cast<const u32x4*>(s_o + 4 * c));
     }
     if (lane < C) {
       const size_t pr = (row0 + lane) * a.max_partitions + j;
-      store_f32<true>(a.part_max + pr, s_o[C * D + lane]);
-      store_f32<true>(a.part_sum + pr, s_o[C * D + C + lane]);
+      store_f32<QKNORM>(a.part_max + pr, s_o[C * D + lane]);
+      store_f32<QKNORM>(a.part_sum + pr, s_o[C * D + C + lane]);
     }
   }
 
   // Log-sum-exp combine of the `pieces` partials of segment seg's C columns
-  // (one wave; weights staged in LDS), done by the combine launch or by the
-  // last piece to arrive, which then clears the counter.  A lane owns float4
-  // pieces of the C rows.
+  // by the last piece to arrive (QK-norm modes; one wave, weights staged in
+  // LDS), which then clears the counter.  A lane owns float4 pieces of the C
+  // rows.
   // The loads of the statistics and of the first batch of partial rows all
   // go out together (one round trip when pieces <= kBatch); a wave that
   // finishes two segments issues both segments' loads before computing
@@ -679,6 +681,77 @@ struct StreamKernel {
     CombineLoads ld;
     combine_issue(a, seg, pieces, ld);
     combine_finish(a, seg, pieces, ld, s_w);
+  }
+
+  // The combine launch's form: every lane keeps a running log-sum-exp of
+  // the float4 pieces it owns in registers (the statistics of its own heads
+  // loaded next to the partial rows, no LDS, no cross-lane step), kOW pieces
+  // per lane and kRW waves per segment.  One wave covers a segment of up to
+  // 128 float4s (C * D <= 512); larger segments take one wave per 64 float4s
+  // (e.g. 8 heads of 128: four waves), which measured faster than fewer
+  // waves with more pieces per lane.
+  static constexpr int kOW = kOwn >= 4 ? 1 : kOwn;
+  static constexpr int kRW = kOwn / kOW;
+  static constexpr int kRB = 16 / kOW;  // partitions per round trip
+
+  static __device__ __forceinline__ void combine_rows(const DecodeArgs& a, int seg, int pieces, int part) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t row0 = seg_row0(a, seg);
+    const int P = a.max_partitions;
+    const __amdgpu_buffer_rsrc_t rs = partial_rows(a, row0);
+    float M[kOW], den[kOW];
+    float4_t num[kOW];
+#pragma unroll
+    for (int k = 0; k < kOW; ++k) {
+      M[k] = -FLT_MAX;
+      den[k] = 0.0f;
+      num[k] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    for (int p0 = 0; p0 < pieces; p0 += kRB) {
+      float mv[kOW][kRB], lv[kOW][kRB];
+      u32x4 v[kOW][kRB];
+#pragma unroll
+      for (int k = 0; k < kOW; ++k) {
+        const int c = (part * kOW + k) * kWave + lane;
+        const int h = c < kF4 ? 4 * c / D : 0;
+        const float* pm = a.part_max + (row0 + h) * P;
+        const float* pl = a.part_sum + (row0 + h) * P;
+#pragma unroll
+        for (int q = 0; q < kRB; ++q) {
+          const bool ok = p0 + q < pieces && c < kF4;
+          mv[k][q] = ok ? pm[p0 + q] : -FLT_MAX;
+          lv[k][q] = ok ? pl[p0 + q] : 0.0f;
+          v[k][q] = ok ? buffer_load16(rs, partial_offset(a, c, p0 + q)) : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kOW; ++k) {
+        float Mn = M[k];
+#pragma unroll
+        for (int q = 0; q < kRB; ++q) Mn = fmaxf(Mn, mv[k][q]);
+        const float r = fast_exp2((M[k] - Mn) * kLog2e);
+        den[k] *= r;
+        num[k] *= r;
+#pragma unroll
+        for (int q = 0; q < kRB; ++q) {
+          const float w = lv[k][q] * fast_exp2((mv[k][q] - Mn) * kLog2e);
+          den[k] += w;
+          num[k] += w * __builtin_bit_cast(float4_t, v[k][q]);
+        }
+        M[k] = Mn;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kOW; ++k) {
+      const int c = (part * kOW + k) * kWave + lane;
+      if (c < kF4) {
+        half4_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (_Float16)(num[k][e] / den[k]);
+        *reinterpret_cast<half4_t*>(static_cast<_Float16*>(a.out) + seg_qrow(a, seg, 4 * c / D) * D +
+                                    4 * c % D) = o;
+      }
+    }
   }
 
   // Two segments finished by the same wave: one round trip for both.
@@ -958,17 +1031,29 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
         static_cast<_Float16*>(a.out)[size_t(b) * K::NQ(a) * a.Hq * D + i] = (_Float16)0.0f;
 }
 
-// The combine launch of the balanced step (modes without QK-norm): segment
-// seg (a grid-stride loop beyond the grid) combines the pieces its counter
-// holds and clears it; 0 = a segment that one wave finished.
+// The combine launch of the balanced step (modes without QK-norm): workgroup
+// seg (a grid-stride loop beyond the grid), kRW waves, combines the pieces
+// segment seg's counter holds and clears it; 0 = a segment that one wave
+// finished.  Partials and counts were written by the attend launch, so plain
+// loads see them.
 template <int D, int C, bool FP8, bool EXT>
-__global__ __launch_bounds__(kWave) void stream_combine_kernel(DecodeArgs a, int nseg) {
+__global__ __launch_bounds__((kWave * StreamKernel<D, C, FP8, kModeCombine, EXT, false>::kRW))
+void stream_combine_kernel(DecodeArgs a, int nseg) {
   using K = StreamKernel<D, C, FP8, kModeCombine, EXT, false>;
-  __shared__ float s_w[2 * C * kMaxStepPartitions];
+  const int part = int(threadIdx.x / kWave);  // this wave's share of the segment
   for (int seg = blockIdx.x; seg < nseg; seg += gridDim.x) {
     const int pieces = __builtin_amdgcn_readfirstlane(int(a.counters[seg]));
-    if (pieces > 0) K::finish(a, seg, pieces, s_w);
+    if (pieces > 0) K::combine_rows(a, seg, pieces, part);
+    // every wave of the workgroup has read the count before it is cleared
+    if constexpr (K::kRW > 1) __syncthreads();
+    if (pieces > 0 && threadIdx.x == 0) a.counters[seg] = 0u;
   }
+}
+
+// Workgroup shape of the combine launch.
+template <int D, int C, bool FP8, bool EXT>
+dim3 combine_block() {
+  return dim3(kWave * StreamKernel<D, C, FP8, kModeCombine, EXT, false>::kRW);
 }
 
 // Compute units of the current device (queried once per device).
@@ -1001,10 +1086,12 @@ hipError_t launch_stream(const DecodeArgs& a, int B, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int nseg = B * a.Hkv * (ext ? a.cgroups : 1);
   if (ext)
-    hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, true>), dim3(min(nseg, 2 * workers)), dim3(kWave),
+    hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, true>), dim3(min(nseg, 2 * workers)),
+                       (combine_block<D, C, FP8, true>()),
                        0, stream, a, nseg);
   else
-    hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, false>), dim3(min(nseg, 2 * workers)), dim3(kWave),
+    hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, false>), dim3(min(nseg, 2 * workers)),
+                       (combine_block<D, C, FP8, false>()),
                        0, stream, a, nseg);
   return hipGetLastError();
 }

@@ -51,13 +51,15 @@ __device__ __forceinline__ float load_uniform_f32(const float* p) {
 // writing back or invalidating whole caches.  Ordinary accesses are used
 // when the handoff happens across launches.
 // 16-byte forms of the same coherent accesses (cache policy sc1, as the
-// agent-scope atomics use), through a buffer resource.
+// agent-scope atomics use), through a buffer resource; store16<false> is the
+// plain store.
 constexpr int kCoherentAux = 16;
-__device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCoherentAux);
-}
 __device__ __forceinline__ u32x4 load16_coherent(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentAux);
+}
+template <bool COHERENT>
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, COHERENT ? kCoherentAux : 0);
 }
 
 template <bool COHERENT>
