@@ -51,22 +51,23 @@ PREFIX_SOURCES = ("decode_stream_prefix.hip", "decode_prefix_impl.h")
 # (in blocks) that the run passed; its hash covers the plain step's sources,
 # and the prefix step's too for a shared-prefix run.
 MEASURED_TRAFFIC = {
-    ("c2", "e2713ccdc7488767", False, 0): {"fetch_bytes": 316679157, "write_bytes": 3340288,
-        "attend_fetch_bytes": 313809899, "combine_fetch_bytes": 2869259,
+    ("c2", "f9f05a5fd15eefa4", False, 0): {"fetch_bytes": 316647808, "write_bytes": 3080192,
+        "attend_fetch_bytes": 313828736, "combine_fetch_bytes": 2819072,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c3", "f8bc02b223875d8f", False, 64): {"fetch_bytes": 590526155, "write_bytes": 9895936,
-        "attend_fetch_bytes": 582510219, "combine_fetch_bytes": 8015936,
+    ("c3", "2ee2400dd51ba7d7", False, 64): {"fetch_bytes": 591076853, "write_bytes": 9240656,
+        "attend_fetch_bytes": 583105013, "combine_fetch_bytes": 7971840,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c3", "e2713ccdc7488767", True, 0): {"fetch_bytes": 570358880, "write_bytes": 6018267,
-        "attend_fetch_bytes": 565859339, "combine_fetch_bytes": 4499541,
+    ("c3", "f9f05a5fd15eefa4", True, 0): {"fetch_bytes": 570425291, "write_bytes": 5805741,
+        "attend_fetch_bytes": 565959627, "combine_fetch_bytes": 4465664,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c4", "e2713ccdc7488767", False, 0): {"fetch_bytes": 4285758955, "write_bytes": 10022144,
-        "attend_fetch_bytes": 4285758955, "combine_fetch_bytes": 0,
+    ("c4", "f9f05a5fd15eefa4", False, 0): {"fetch_bytes": 4285481515, "write_bytes": 10022176,
+        "attend_fetch_bytes": 4285481515, "combine_fetch_bytes": 0,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c5", "e2713ccdc7488767", False, 0): {"fetch_bytes": 563737515, "write_bytes": 12840965,
-        "attend_fetch_bytes": 552566624, "combine_fetch_bytes": 11170891,
+    ("c5", "f9f05a5fd15eefa4", False, 0): {"fetch_bytes": 563638485, "write_bytes": 11798899,
+        "attend_fetch_bytes": 552572117, "combine_fetch_bytes": 11066368,
         "source": "profiles/step_hbm_bytes.md"},
 }
+
 
 def code_of(text):
     """A source's code without its // comments and blank lines (so that a
