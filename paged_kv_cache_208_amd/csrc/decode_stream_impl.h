@@ -190,8 +190,11 @@ __device__ __forceinline__ void advance(Cursor& c, const DecodeArgs& a, int B, i
   c.f = first_tile(c.L, W);
 }
 
+// 115: measured on the 70B-shaped E4M3 batch with the lane-local combine
+// launch (100 to 150 swept; 110 and 120 run 0.3-0.8 us slower, 100 and 135
+// 1-1.5 us slower).
 #ifndef PKV_STREAM_SKEW_FP8
-#define PKV_STREAM_SKEW_FP8 120
+#define PKV_STREAM_SKEW_FP8 115
 #endif
 
 // The wave ranges, back to back in the flattened order, in nblk blocks of
