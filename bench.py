@@ -51,22 +51,23 @@ PREFIX_SOURCES = ("decode_stream_prefix.hip", "decode_prefix_impl.h")
 # (in blocks) that the run passed; its hash covers the plain step's sources,
 # and the prefix step's too for a shared-prefix run.
 MEASURED_TRAFFIC = {
-    ("c2", "f9f05a5fd15eefa4", False, 0): {"fetch_bytes": 316647808, "write_bytes": 3080192,
-        "attend_fetch_bytes": 313828736, "combine_fetch_bytes": 2819072,
+    ("c2", "5b75ce336008c914", False, 0): {"fetch_bytes": 316696747, "write_bytes": 3080192,
+        "attend_fetch_bytes": 313877675, "combine_fetch_bytes": 2819072,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c3", "2ee2400dd51ba7d7", False, 64): {"fetch_bytes": 591076853, "write_bytes": 9240656,
-        "attend_fetch_bytes": 583105013, "combine_fetch_bytes": 7971840,
+    ("c3", "0a126906bb6fae7f", False, 64): {"fetch_bytes": 591518091, "write_bytes": 9240613,
+        "attend_fetch_bytes": 583546251, "combine_fetch_bytes": 7971840,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c3", "f9f05a5fd15eefa4", True, 0): {"fetch_bytes": 570425291, "write_bytes": 5805741,
-        "attend_fetch_bytes": 565959627, "combine_fetch_bytes": 4465664,
+    ("c3", "5b75ce336008c914", True, 0): {"fetch_bytes": 570149931, "write_bytes": 5802085,
+        "attend_fetch_bytes": 565684267, "combine_fetch_bytes": 4465664,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c4", "f9f05a5fd15eefa4", False, 0): {"fetch_bytes": 4285481515, "write_bytes": 10022176,
-        "attend_fetch_bytes": 4285481515, "combine_fetch_bytes": 0,
+    ("c4", "5b75ce336008c914", False, 0): {"fetch_bytes": 4285612373, "write_bytes": 10022160,
+        "attend_fetch_bytes": 4285612373, "combine_fetch_bytes": 0,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c5", "f9f05a5fd15eefa4", False, 0): {"fetch_bytes": 563638485, "write_bytes": 11798899,
-        "attend_fetch_bytes": 552572117, "combine_fetch_bytes": 11066368,
+    ("c5", "5b75ce336008c914", False, 0): {"fetch_bytes": 563650411, "write_bytes": 11796651,
+        "attend_fetch_bytes": 552584043, "combine_fetch_bytes": 11066368,
         "source": "profiles/step_hbm_bytes.md"},
 }
+
 
 
 def code_of(text):
