@@ -12,8 +12,9 @@
 // Ranges), and the waves of one XCD take one contiguous block of ranges: an
 // XCD reads about one kv head's tiles, so the blocks that several sequences
 // share (a common prefix) are re-read through that XCD's own L2, and the
-// pieces of a split segment are combined within one XCD.  Every wave therefore moves about the same
-// number of bytes, whatever the mix of context lengths, and streams straight
+// pieces of a split segment mostly come from one XCD.  Every wave therefore
+// moves about the same number of bytes, whatever the mix of context
+// lengths, and streams straight
 // across the boundaries between (sequence, kv head) segments: the next
 // tile's loads are issued before the current tile is computed, whichever
 // segment it belongs to.
@@ -22,7 +23,8 @@
 // normalised output is written directly).  A segment shared by several
 // consecutive waves leaves one partial (m, l, o) per wave, combined
 // (log-sum-exp, as paged_attn_reduce does) by the combine launch, which
-// reads the piece count the segment's first piece left in its counter.
+// reads the piece count the segment's first piece left in its counter; each
+// of its lanes keeps a running log-sum-exp of its own float4s of the rows.
 // With QK-norm the last wave to finish its piece combines them in the same
 // launch (and writes q' back), counting arrivals with device-scope coherent
 // accesses.  The counters return to zero either way.
