@@ -164,6 +164,10 @@ def parse():
                         "per sequence into E4M3 blocks (use an E4M3 config, c5)")
     p.add_argument("--copy-pairs", type=int, default=2048,
                    help="block pairs per copy-blocks launch")
+    p.add_argument("--steady-steps", type=int, default=2000,
+                   help="after the timed passes, also time this many back-to-back steps after\n"
+                        "--steady-warmup more (reported as steady_state, not as value; 0 = skip)")
+    p.add_argument("--steady-warmup", type=int, default=500)
     p.add_argument("--read-ceiling-mib", type=int, default=1024,
                    help="after timing, read a buffer of this many MiB with the library's "
                         "streaming-read kernel and report the step's rate against it "
@@ -637,6 +641,23 @@ def main():
         torch.cuda.synchronize()
         return s0.elapsed_time(s1) / K
 
+    # steady state: a longer run after the timed passes (the first ~10-30 ms
+    # of sustained work after the process starts run slower, and a short
+    # window also carries its first launch's host latency); reported beside
+    # `value`, which stays the W / K window's
+    steady_ms = None
+    if args.steady_steps > 0:
+        for i in range(args.steady_warmup):
+            step(i)
+        torch.cuda.synchronize()
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record(stream)
+        for i in range(args.steady_steps):
+            step(i)
+        q1.record(stream)
+        torch.cuda.synchronize()
+        steady_ms = q0.elapsed_time(q1) / args.steady_steps
+
     # the step's practical read ceiling: its tiles, in its order and split,
     # read with its cache policies and nothing computed (pkv_tile_read)
     tile_ms = None
@@ -778,6 +799,11 @@ def main():
         "pct_of_tile_read_ceiling": (None if tile_ms is None
                                      else round(100 * tile_ms / kernel_ms, 2)),
         "paging": paging,
+        "steady_state": None if steady_ms is None else {
+            "warmup": args.steady_warmup, "steps": args.steady_steps,
+            "ms_per_step": round(steady_ms, 5),
+            "unique_kv_gbps": round(kv_unique / (steady_ms * 1e-3) / 1e9, 2),
+            "frac_of_hbm_peak": round(kv_unique / (steady_ms * 1e-3) / 1e9 / HBM_GBPS, 4)},
         "kv_bytes_per_step": kv,
         "unique_kv_bytes_per_step": kv_unique,
         "unique_kv_gbps": round(unique_rate, 2),
