@@ -87,13 +87,16 @@ def strerror(status: int) -> str:
     return lib().pkv_strerror(int(status)).decode()
 
 
+# Device pointers and streams go over as plain integers: every pointer
+# argument is declared c_void_p, which ctypes converts from an int (or None)
+# itself, at a fraction of the cost of building c_void_p objects per call.
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return s.cuda_stream
 
 
 def _check(t, name, dtype, ndim=None):
