@@ -22,7 +22,12 @@ ARCH = "gfx950"
 
 # Packed-fp32 VALU forms stay off: the compiler would otherwise form
 # v_pk_{add,mul,fma}_f32 from scalar float code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# -amdgpu-kernarg-preload-count: the first three kernel arguments arrive in
+# SGPRs at dispatch (the step kernels put the lengths pointer, the batch size
+# and the wave count there, so their first load needs no load of the
+# argument block); a kernel whose first argument is a struct preloads nothing.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-kernarg-preload-count=3"]
 
 
 def hipcc():

@@ -365,7 +365,7 @@ struct PrefixKernel {
 
 template <int D, int C, bool FP8, int MODE, bool EXT>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<FP8>(), 8)))
-void decode_prefix_kernel(DecodeArgs a, int B, int workers) {
+void decode_prefix_kernel(const int32_t* __restrict__ lens, int B, int workers, DecodeArgs a) {
   using P = PrefixKernel<D, C, FP8, MODE, EXT>;
   using K = typename P::K;
   using Geo = MfmaGeo<D, FP8>;
@@ -384,7 +384,7 @@ void decode_prefix_kernel(DecodeArgs a, int B, int workers) {
   pg.Tp = a.prefix_tiles;
   pg.spp = P::kSpp;
   pg.NG = (B + P::kSpp - 1) / P::kSpp;
-  const int L0 = lane < B ? a.context_lens[lane] : 0;
+  const int L0 = lane < B ? lens[lane] : 0;  // lens = a.context_lens, preloaded
   const Totals tot = p_totals(a, B, L0, pg);
   pg.wh = tot.per_head;
   const int64_t W = tot.tiles;
@@ -495,10 +495,10 @@ hipError_t launch_prefix(const DecodeArgs& a, int B, hipStream_t stream) {
   const int workers = device_cus() * 4 * stream_waves_per_eu<FP8>();
   if (a.bs_tiles > 1)
     hipLaunchKernelGGL((decode_prefix_kernel<D, C, FP8, MODE, true>), dim3(workers), dim3(kWave), 0,
-                       stream, a, B, workers);
+                       stream, a.context_lens, B, workers, a);
   else
     hipLaunchKernelGGL((decode_prefix_kernel<D, C, FP8, MODE, false>), dim3(workers), dim3(kWave), 0,
-                       stream, a, B, workers);
+                       stream, a.context_lens, B, workers, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nseg = B * a.Hkv;
@@ -506,7 +506,7 @@ hipError_t launch_prefix(const DecodeArgs& a, int B, hipStream_t stream) {
   // segment, nq = 1, so the plain layout applies
   hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, false>), dim3(min(nseg, 2 * workers)),
                      (combine_block<D, C, FP8, false>()),
-                     0, stream, a, nseg);
+                     0, stream, a.counters, nseg, a);
   return hipGetLastError();
 }
 

@@ -772,7 +772,7 @@ struct StreamKernel {
 
 template <int D, int C, bool FP8, int MODE, bool EXT, bool CACHED>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<FP8>(), 8)))
-void decode_stream_kernel(DecodeArgs a, int B, int workers) {
+void decode_stream_kernel(const int32_t* __restrict__ lens, int B, int workers, DecodeArgs a) {
   using K = StreamKernel<D, C, FP8, MODE, EXT, CACHED>;
   // without QK-norm the pieces of split segments are combined by a second
   // launch (stream_combine_kernel); with it, by the piece that arrives last
@@ -805,7 +805,10 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
   __shared__ float s_gq[K::QKNORM ? D : 1];          // RMSNorm weights of q and k
   __shared__ float s_gk[K::QKNORM ? D : 1];
 
-  const int L0 = lane < B ? a.context_lens[lane] : 0;
+  // lens (= a.context_lens), B and workers lead the argument list, so that
+  // the build preloads them into SGPRs at dispatch and the lengths load goes
+  // out before any load of the argument block
+  const int L0 = lane < B ? lens[lane] : 0;
   const Totals tot = total_tiles(a, B, L0, win, K::CG(a));
   const int64_t W = tot.tiles;
   // equal shares, but long enough that no sequence's segment is cut into more
@@ -1043,15 +1046,15 @@ void decode_stream_kernel(DecodeArgs a, int B, int workers) {
 // loads see them.
 template <int D, int C, bool FP8, bool EXT>
 __global__ __launch_bounds__((kWave * StreamKernel<D, C, FP8, kModeCombine, EXT, false>::kRW))
-void stream_combine_kernel(DecodeArgs a, int nseg) {
+void stream_combine_kernel(uint32_t* __restrict__ counters, int nseg, DecodeArgs a) {
   using K = StreamKernel<D, C, FP8, kModeCombine, EXT, false>;
   const int part = int(threadIdx.x / kWave);  // this wave's share of the segment
   for (int seg = blockIdx.x; seg < nseg; seg += gridDim.x) {
-    const int pieces = __builtin_amdgcn_readfirstlane(int(a.counters[seg]));
+    const int pieces = __builtin_amdgcn_readfirstlane(int(counters[seg]));
     if (pieces > 0) K::combine_rows(a, seg, pieces, part);
     // every wave of the workgroup has read the count before it is cleared
     if constexpr (K::kRW > 1) __syncthreads();
-    if (pieces > 0 && threadIdx.x == 0) a.counters[seg] = 0u;
+    if (pieces > 0 && threadIdx.x == 0) counters[seg] = 0u;
   }
 }
 
@@ -1082,10 +1085,10 @@ hipError_t launch_stream(const DecodeArgs& a, int B, hipStream_t stream) {
   const bool ext = a.window > 0 || a.nq > 1 || a.bs_tiles > 1;
   if (ext)
     hipLaunchKernelGGL((decode_stream_kernel<D, C, FP8, MODE, true, CACHED>), dim3(workers),
-                       dim3(kWave), 0, stream, a, B, workers);
+                       dim3(kWave), 0, stream, a.context_lens, B, workers, a);
   else
     hipLaunchKernelGGL((decode_stream_kernel<D, C, FP8, MODE, false, CACHED>), dim3(workers),
-                       dim3(kWave), 0, stream, a, B, workers);
+                       dim3(kWave), 0, stream, a.context_lens, B, workers, a);
   if constexpr ((MODE & kModeQkNorm) != 0) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1093,11 +1096,11 @@ hipError_t launch_stream(const DecodeArgs& a, int B, hipStream_t stream) {
   if (ext)
     hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, true>), dim3(min(nseg, 2 * workers)),
                        (combine_block<D, C, FP8, true>()),
-                       0, stream, a, nseg);
+                       0, stream, a.counters, nseg, a);
   else
     hipLaunchKernelGGL((stream_combine_kernel<D, C, FP8, false>), dim3(min(nseg, 2 * workers)),
                        (combine_block<D, C, FP8, false>()),
-                       0, stream, a, nseg);
+                       0, stream, a.counters, nseg, a);
   return hipGetLastError();
 }
 
