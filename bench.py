@@ -51,22 +51,23 @@ PREFIX_SOURCES = ("decode_stream_prefix.hip", "decode_prefix_impl.h")
 # (in blocks) that the run passed; its hash covers the plain step's sources,
 # and the prefix step's too for a shared-prefix run.
 MEASURED_TRAFFIC = {
-    ("c2", "5b75ce336008c914", False, 0): {"fetch_bytes": 316696747, "write_bytes": 3080192,
-        "attend_fetch_bytes": 313877675, "combine_fetch_bytes": 2819072,
+    ("c2", "a3378f8d27623030", False, 0): {"fetch_bytes": 316610251, "write_bytes": 3080192,
+        "attend_fetch_bytes": 313798347, "combine_fetch_bytes": 2811904,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c3", "0a126906bb6fae7f", False, 64): {"fetch_bytes": 591518091, "write_bytes": 9240613,
-        "attend_fetch_bytes": 583546251, "combine_fetch_bytes": 7971840,
+    ("c3", "aca093285485677a", False, 64): {"fetch_bytes": 592490944, "write_bytes": 9240576,
+        "attend_fetch_bytes": 584521152, "combine_fetch_bytes": 7969792,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c3", "5b75ce336008c914", True, 0): {"fetch_bytes": 570149931, "write_bytes": 5802085,
-        "attend_fetch_bytes": 565684267, "combine_fetch_bytes": 4465664,
+    ("c3", "a3378f8d27623030", True, 0): {"fetch_bytes": 570523627, "write_bytes": 5795203,
+        "attend_fetch_bytes": 566065131, "combine_fetch_bytes": 4458496,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c4", "5b75ce336008c914", False, 0): {"fetch_bytes": 4285612373, "write_bytes": 10022160,
-        "attend_fetch_bytes": 4285612373, "combine_fetch_bytes": 0,
+    ("c4", "a3378f8d27623030", False, 0): {"fetch_bytes": 4285652896, "write_bytes": 10022176,
+        "attend_fetch_bytes": 4285652896, "combine_fetch_bytes": 0,
         "source": "profiles/step_hbm_bytes.md"},
-    ("c5", "5b75ce336008c914", False, 0): {"fetch_bytes": 563650411, "write_bytes": 11796651,
-        "attend_fetch_bytes": 552584043, "combine_fetch_bytes": 11066368,
+    ("c5", "a3378f8d27623030", False, 0): {"fetch_bytes": 563634560, "write_bytes": 11803403,
+        "attend_fetch_bytes": 552571264, "combine_fetch_bytes": 11063296,
         "source": "profiles/step_hbm_bytes.md"},
 }
+
 
 
 
