@@ -189,12 +189,13 @@ def _relen(d, lens):
     return dict(d, context_lens=lens, slot_mapping=slots)
 
 
+@pytest.mark.parametrize("B", [100, 300])
 @pytest.mark.parametrize("splits", [3, 16])
-def test_step_balanced_many_short_sequences(splits):
-    """More sequences than one wave scans at once (B > 64), segments of 1-3
-    tiles so one wave's range holds many segments, every fifth sequence
-    empty."""
-    cfg, d = batch("c2", B=100, len_lo=1, len_hi=48, mbs=3)
+def test_step_balanced_many_short_sequences(splits, B):
+    """More sequences than one wave scans at once (B > 64, up to five
+    chunks of 64 lengths), segments of 1-3 tiles so one wave's range holds
+    many segments, every fifth sequence empty."""
+    cfg, d = batch("c2", B=B, len_lo=1, len_hi=48, mbs=3)
     lens = d["context_lens"].copy()
     lens[::5] = 0
     d2 = _relen(d, lens)

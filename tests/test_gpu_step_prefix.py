@@ -125,3 +125,20 @@ def test_prefix_empty_sequences_and_smallest_piece_budget():
     err = _check(cfg, d2, out, g)
     assert err <= TOL_F16
     assert torch.all(out[empty] == 0)
+
+
+def test_prefix_more_sequences_than_four_length_chunks():
+    """B = 300: five chunks of 64 lengths in the scans that place each
+    wave's range, with every seventh sequence empty."""
+    cfg, d = batch("c3", B=300, prefix_tokens=32, len_lo=1, len_hi=100, mbs=9, seed=208_650)
+    lens = d["context_lens"].copy()
+    empty = list(range(0, 300, 7))
+    lens[empty] = 0
+    slots = d["slot_mapping"].copy()
+    slots[empty] = -1
+    d2 = dict(d, context_lens=lens, slot_mapping=slots)
+    g = to_device(d2)
+    out = _run(cfg, g, prefix_blocks=2, P=6)
+    err = _check(cfg, d2, out, g)
+    assert err <= TOL_F16
+    assert torch.all(out[empty] == 0)
